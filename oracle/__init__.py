@@ -1,0 +1,167 @@
+"""CPU oracle for the routed-expert MoE forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product path (the HIP library and
+its Python binding) never loads it and shares no code with it.
+
+Thin numpy/ctypes wrappers over ``moe_oracle.cpp``; every wrapper names the
+C function it calls. Arrays are host numpy arrays. 16-bit inputs are passed
+as ``uint16`` bit patterns (or numpy ``float16`` for fp16); fp32 as float32.
+
+Dtype codes: 0 = fp16, 1 = bf16, 2 = fp32.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F16, BF16, F32 = 0, 1, 2
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        L.oracle_to_f32.argtypes = [i32, vp, f32p, i64]
+        L.oracle_from_f32.argtypes = [i32, f32p, vp, i64]
+        L.oracle_silu_mul.argtypes = [f32p, f32p, f32p, i64]
+        L.oracle_num_blocks.argtypes = [i32, i32, i32, i32]
+        L.oracle_num_blocks.restype = i64
+        L.oracle_dispatch.argtypes = [i32p, f32p, i32, i32, i32, i32] + [vp] * 8
+        L.oracle_dispatch.restype = i64
+        L.oracle_expert_pair.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, f32p, f32p]
+        L.oracle_moe_forward.argtypes = [i32, vp, vp, vp, vp, i32p, f32p, i32, i32, i32,
+                                         i32, i32, i32p, i32, f32p, f32p, f32p]
+        L.oracle_reduce.argtypes = [i32, vp, i64, i32p, f32p, i32, i32, i32, f32p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _storage(a, dt):
+    """Contiguous storage array for dtype code dt (uint16 bits or float32)."""
+    if dt == F32:
+        return _c(a, np.float32)
+    if a.dtype == np.float16:
+        return _c(a, np.float16).view(np.uint16)
+    return _c(a, np.uint16)
+
+
+def to_f32(bits, dt):
+    """oracle_to_f32: storage -> fp32 (exact widening)."""
+    s = _storage(np.asarray(bits), dt)
+    out = np.empty(s.shape, np.float32)
+    assert lib().oracle_to_f32(dt, _ptr(s), _ptr(out), s.size) == 0
+    return out
+
+
+def from_f32(x, dt):
+    """oracle_from_f32: fp32 -> storage (round to nearest even); uint16 bits for 16-bit."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.float32 if dt == F32 else np.uint16)
+    assert lib().oracle_from_f32(dt, _ptr(x), _ptr(out), x.size) == 0
+    return out
+
+
+def silu_mul(g, u):
+    """oracle_silu_mul: SiLU(g) * u in fp32."""
+    g, u = _c(g, np.float32), _c(u, np.float32)
+    out = np.empty(g.shape, np.float32)
+    lib().oracle_silu_mul(_ptr(g), _ptr(u), _ptr(out), g.size)
+    return out
+
+
+def num_blocks(T, K, E, BM):
+    return int(lib().oracle_num_blocks(T, K, E, BM))
+
+
+def dispatch(ids, w, E, BM):
+    """oracle_dispatch: expert-sorted tables for ids/w of shape [T, K].
+
+    Returns a dict of numpy arrays plus ``n_valid``; raises on invalid ids.
+    """
+    ids = _c(ids, np.int32)
+    T, K = ids.shape
+    w = None if w is None else _c(w, np.float32)
+    P = T * K
+    nb = num_blocks(T, K, E, BM)
+    out = dict(
+        group_sizes=np.empty(E, np.int32), group_offsets=np.empty(E, np.int32),
+        group_padded_offsets=np.empty(E, np.int32), block_expert=np.empty(nb, np.int32),
+        sorted_pair=np.empty(P, np.int32), sorted_token=np.empty(P, np.int32),
+        sorted_weight=np.empty(P, np.float32), token_topk_to_pos=np.empty(P, np.int32))
+    n = lib().oracle_dispatch(
+        _ptr(ids), _ptr(w), T, K, E, BM, _ptr(out["group_sizes"]), _ptr(out["group_offsets"]),
+        _ptr(out["group_padded_offsets"]), _ptr(out["block_expert"]), _ptr(out["sorted_pair"]),
+        _ptr(out["sorted_token"]), _ptr(out["sorted_weight"]), _ptr(out["token_topk_to_pos"]))
+    if n < 0:
+        raise ValueError("oracle_dispatch rejected its arguments")
+    out["n_valid"] = int(n)
+    out["token_topk_to_pos"] = out["token_topk_to_pos"].reshape(T, K)
+    return out
+
+
+def expert_pair(dt, x, wg, wu, wd, token, expert):
+    """oracle_expert_pair: (h [D], expert_out [H]) of one pair, fp32 after rounding."""
+    x, wg, wu, wd = (_storage(a, dt) for a in (x, wg, wu, wd))
+    H = x.shape[-1]
+    D = wg.shape[1]
+    h = np.empty(D, np.float32)
+    eo = np.empty(H, np.float32)
+    rc = lib().oracle_expert_pair(dt, _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), int(token),
+                                  int(expert), H, D, _ptr(h), _ptr(eo))
+    assert rc == 0
+    return h, eo
+
+
+def moe_forward(dt, x, wg, wu, wd, ids, w, tokens=None, want_pairs=False):
+    """oracle_moe_forward: y [n_tokens, H] fp32 (and per-slot h / expert_out).
+
+    x [T, H]; wg, wu [E, D, H]; wd [E, H, D] (storage of dtype dt);
+    ids int32 [T, K]; w fp32 [T, K]; tokens: optional token subset.
+    """
+    x, wg, wu, wd = (_storage(a, dt) for a in (x, wg, wu, wd))
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    T, H = x.shape
+    E, D, _ = wg.shape
+    K = ids.shape[1]
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tok is None else tok.size
+    y = np.empty((n, H), np.float32)
+    hp = np.empty((n * K, D), np.float32) if want_pairs else None
+    ep = np.empty((n * K, H), np.float32) if want_pairs else None
+    rc = lib().oracle_moe_forward(dt, _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(ids), _ptr(w),
+                                  T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
+    if rc != 0:
+        raise ValueError("oracle_moe_forward rejected its arguments")
+    return (y, hp, ep) if want_pairs else y
+
+
+def reduce(dt, X, pos, w=None):
+    """oracle_reduce: y [T, H] fp32 = sum_k w[t,k] * X[pos[t,k]] over pos >= 0."""
+    X = _storage(X, dt)
+    pos = _c(pos, np.int32)
+    T, K = pos.shape
+    R, H = X.shape
+    w = None if w is None else _c(w, np.float32)
+    y = np.empty((T, H), np.float32)
+    rc = lib().oracle_reduce(dt, _ptr(X), R, _ptr(pos), _ptr(w), T, K, H, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_reduce rejected its arguments")
+    return y

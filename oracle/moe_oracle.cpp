@@ -1,0 +1,359 @@
+// moe_oracle.cpp -- plain, slow CPU oracle for the routed-expert MoE forward.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing on the product path may load this file's
+// library: only the tests, the smoke entry point and the benchmark's CPU
+// baseline leg use it. It shares no code, header, table or helper with the HIP
+// library; it includes only the C++ standard library and OpenMP.
+//
+// What it computes (sources, by page title and section):
+//   [A] "tilelang baseline" MoE walkthrough (devpress.csdn.net, tilelang-metax
+//       race): section "forward" (expert sort, counts, offsets, padded offsets,
+//       block->expert table), section "stage-1 gate+up" (SiLU(gate)*up),
+//       section "stage-2 down".
+//   [B] TileLang tutorial ch.18 "End-to-end II", skeletons.py,
+//       moe_routed_kernel docstring (the dispatch contract) and body.
+//   [C] TileOPs-Metax PR #55 "moe_reduce_fused", section 1 (optimisation plan:
+//       fp32 accumulation, K order kept, pos < 0 skipped) and section 2
+//       (reference semantics, with_weights=False means all-ones weights).
+//
+// Precision: the pages fix fp32 accumulation ([A] stage-1/2 accum dtype,
+// [C] section 1), so every dot product and the weighted sum accumulate in
+// fp32 with fused multiply-add, in ascending index order. The intermediates
+// h = SiLU(g)*u and expert_out are tensors of the activation dtype in [B]
+// (UpLogits / Output), so for 16-bit dtypes they are rounded
+// (round-to-nearest-even) to that dtype at exactly those two points. With the
+// fp32 dtype no rounding happens. The output y is returned in fp32.
+//
+// Parity pins for every exported function live in the CPU test-suite: a
+// dense fp64 brute force without any dispatch, closed forms, invariants and
+// the worked table examples of [A]. See oracle/__init__.py for the loader.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <vector>
+
+namespace {
+
+// Storage codes of this file (an interface agreement with the tests only).
+constexpr int kF16 = 0;
+constexpr int kBF16 = 1;
+constexpr int kF32 = 2;
+
+// ---------------------------------------------------------------- dtypes ---
+
+// bfloat16 is the top half of an IEEE binary32; widening is exact.
+float bf16_bits_to_float(uint16_t b) {
+  uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// binary32 -> bfloat16, round to nearest, ties to even. NaN stays NaN (quiet).
+uint16_t float_to_bf16_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  }
+  uint32_t keep = u >> 16;
+  uint32_t rest = u & 0xffffu;
+  if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;
+  return static_cast<uint16_t>(keep);
+}
+
+// IEEE binary16 -> binary32 (exact), written from the format definition:
+// 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+float f16_bits_to_float(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int expo = (h >> 10) & 0x1f;
+  const int frac = h & 0x3ff;
+  float v;
+  if (expo == 0) {
+    v = std::ldexp(static_cast<float>(frac), -24);          // subnormal / zero
+  } else if (expo == 31) {
+    v = frac ? std::numeric_limits<float>::quiet_NaN()
+             : std::numeric_limits<float>::infinity();
+  } else {
+    v = std::ldexp(static_cast<float>(frac | 0x400), expo - 25);
+  }
+  return sign ? -v : v;
+}
+
+// binary32 -> binary16, round to nearest, ties to even; overflow -> inf.
+uint16_t float_to_f16_bits(float f) {
+  const uint16_t sign = std::signbit(f) ? 0x8000u : 0u;
+  if (std::isnan(f)) return static_cast<uint16_t>(sign | 0x7e00u);
+  if (std::isinf(f)) return static_cast<uint16_t>(sign | 0x7c00u);
+  const double a = std::fabs(static_cast<double>(f));
+  if (a == 0.0) return sign;
+  if (a < std::ldexp(1.0, -14)) {
+    // Subnormal range: value = q * 2^-24 with integer q in [0, 1024].
+    double q = std::nearbyint(a * std::ldexp(1.0, 24));    // ties to even
+    return static_cast<uint16_t>(sign | static_cast<uint16_t>(q));
+  }
+  int e2;
+  std::frexp(a, &e2);               // a = m * 2^e2, m in [0.5, 1)
+  int unb = e2 - 1;                 // a in [2^unb, 2^(unb+1))
+  double q = std::nearbyint(a * std::ldexp(1.0, 10 - unb));  // [1024, 2048]
+  if (q >= 2048.0) { q = 1024.0; unb += 1; }
+  if (unb > 15) return static_cast<uint16_t>(sign | 0x7c00u);
+  const int biased = unb + 15;
+  return static_cast<uint16_t>(sign | (biased << 10) | (static_cast<int>(q) - 1024));
+}
+
+float load_elem(int dt, const void* base, int64_t i) {
+  if (dt == kF32) return static_cast<const float*>(base)[i];
+  const uint16_t b = static_cast<const uint16_t*>(base)[i];
+  return dt == kBF16 ? bf16_bits_to_float(b) : f16_bits_to_float(b);
+}
+
+// Rounding of an fp32 value to the storage dtype and back ("mirror" rounding
+// of the intermediates; identity for fp32).
+float round_to(int dt, float v) {
+  if (dt == kBF16) return bf16_bits_to_float(float_to_bf16_bits(v));
+  if (dt == kF16) return f16_bits_to_float(float_to_f16_bits(v));
+  return v;
+}
+
+bool dtype_ok(int dt) { return dt == kF16 || dt == kBF16 || dt == kF32; }
+
+// SiLU(g) = g * sigmoid(g) = g / (1 + e^-g). [A] stage-1 writes sigmoid with
+// exp2(-g*log2 e); the value is the same function, written here with expf.
+float silu(float g) { return g / (1.0f + std::exp(-g)); }
+
+// One routed pair: token row x_t against expert e.
+//   g_j  = sum_h Wg[e,j,h] x[h]         u_j = sum_h Wu[e,j,h] x[h]
+//   h_j  = R(SiLU(g_j) * u_j)                    ([A] stage-1 epilogue)
+//   eo_c = R(sum_j Wd[e,c,j] h_j)                ([A] stage-2, unweighted)
+// W_gate/W_up are [E, D, H] and W_down is [E, H, D], row-major, so each dot
+// product walks a contiguous row ([A] "forward": stacked expert weights).
+void expert_pair(int dt, const float* xrow, const void* wg, const void* wu,
+                 const void* wd, int e, int H, int D, float* hbuf, float* eo) {
+  for (int j = 0; j < D; ++j) {
+    const int64_t row = (static_cast<int64_t>(e) * D + j) * H;
+    float g = 0.0f, u = 0.0f;
+    for (int k = 0; k < H; ++k) {
+      g = std::fma(load_elem(dt, wg, row + k), xrow[k], g);
+      u = std::fma(load_elem(dt, wu, row + k), xrow[k], u);
+    }
+    hbuf[j] = round_to(dt, silu(g) * u);
+  }
+  for (int c = 0; c < H; ++c) {
+    const int64_t row = (static_cast<int64_t>(e) * H + c) * D;
+    float o = 0.0f;
+    for (int j = 0; j < D; ++j) o = std::fma(load_elem(dt, wd, row + j), hbuf[j], o);
+    eo[c] = round_to(dt, o);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// ------------------------------------------------------------ conversions --
+// Element-wise storage conversions, exported so the tests can pin them
+// against library conversions and hand-made tie cases.
+int oracle_to_f32(int dt, const void* in, float* out, int64_t n) {
+  if (!dtype_ok(dt)) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = load_elem(dt, in, i);
+  return 0;
+}
+
+int oracle_from_f32(int dt, const float* in, void* out, int64_t n) {
+  if (!dtype_ok(dt)) return -1;
+  for (int64_t i = 0; i < n; ++i) {
+    if (dt == kF32) static_cast<float*>(out)[i] = in[i];
+    else if (dt == kBF16) static_cast<uint16_t*>(out)[i] = float_to_bf16_bits(in[i]);
+    else static_cast<uint16_t*>(out)[i] = float_to_f16_bits(in[i]);
+  }
+  return 0;
+}
+
+int oracle_silu_mul(const float* g, const float* u, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = silu(g[i]) * u[i];
+  return 0;
+}
+
+// ------------------------------------------------------------- dispatch ----
+// Number of row blocks: ceil(P / BM) + E with P = T*K, counted over every
+// slot even when some are masked ([A] "forward", kernel grid size M).
+int64_t oracle_num_blocks(int T, int K, int E, int BM) {
+  const int64_t P = static_cast<int64_t>(T) * K;
+  return (P + BM - 1) / BM + E;
+}
+
+// Expert-sorted dispatch ([A] "forward" steps 2-5; [B] dispatch contract).
+//   * pairs p = t*K + k are grouped by expert, stable in p (the page's
+//     argsort leaves ties unspecified; a stable counting sort is the reading
+//     taken here);
+//   * a slot whose id is negative is masked: it is not counted, and its
+//     position is -1 (it is then skipped by the reduce, [C] section 1);
+//   * group_offsets = exclusive prefix sum of group_sizes;
+//   * group_padded_offsets[0] = 0 and
+//     group_padded_offsets[e] = group_padded_offsets[e-1]
+//                               + ceil((group_sizes[e-1] + 1) / BM) * BM;
+//   * block_expert[bx] = the last expert e with group_padded_offsets[e] <= bx*BM.
+// Returns the number of valid pairs, or -1 when an id is >= E or an argument
+// is out of range. Entries of the sorted arrays past the valid count are set
+// to -1 (pair, token) and 0 (weight).
+int64_t oracle_dispatch(const int32_t* ids, const float* w, int T, int K, int E,
+                        int BM, int32_t* group_sizes, int32_t* group_offsets,
+                        int32_t* group_padded_offsets, int32_t* block_expert,
+                        int32_t* sorted_pair, int32_t* sorted_token,
+                        float* sorted_weight, int32_t* pos) {
+  if (T < 0 || K <= 0 || E <= 0 || BM <= 0) return -1;
+  const int64_t P = static_cast<int64_t>(T) * K;
+  for (int64_t p = 0; p < P; ++p) {
+    if (ids[p] >= E) return -1;
+  }
+  std::vector<int64_t> cnt(E, 0);
+  for (int64_t p = 0; p < P; ++p) {
+    if (ids[p] >= 0) cnt[ids[p]] += 1;
+  }
+  std::vector<int64_t> off(E, 0);
+  for (int e = 1; e < E; ++e) off[e] = off[e - 1] + cnt[e - 1];
+  int64_t n_valid = 0;
+  for (int e = 0; e < E; ++e) n_valid += cnt[e];
+
+  std::vector<int64_t> fill(E, 0);
+  for (int64_t p = 0; p < P; ++p) {
+    const int e = ids[p];
+    if (e < 0) {
+      pos[p] = -1;
+      continue;
+    }
+    const int64_t i = off[e] + fill[e]++;
+    sorted_pair[i] = static_cast<int32_t>(p);
+    sorted_token[i] = static_cast<int32_t>(p / K);
+    sorted_weight[i] = w ? w[p] : 1.0f;
+    pos[p] = static_cast<int32_t>(i);
+  }
+  for (int64_t i = n_valid; i < P; ++i) {
+    sorted_pair[i] = -1;
+    sorted_token[i] = -1;
+    sorted_weight[i] = 0.0f;
+  }
+
+  std::vector<int64_t> padded(E, 0);
+  for (int e = 1; e < E; ++e) {
+    const int64_t need = cnt[e - 1] + 1;
+    padded[e] = padded[e - 1] + ((need + BM - 1) / BM) * BM;
+  }
+  for (int e = 0; e < E; ++e) {
+    group_sizes[e] = static_cast<int32_t>(cnt[e]);
+    group_offsets[e] = static_cast<int32_t>(off[e]);
+    group_padded_offsets[e] = static_cast<int32_t>(padded[e]);
+  }
+  const int64_t nblk = oracle_num_blocks(T, K, E, BM);
+  for (int64_t bx = 0; bx < nblk; ++bx) {
+    const int64_t start = bx * BM;
+    int owner = 0;
+    for (int e = 0; e < E; ++e) {
+      if (padded[e] <= start) owner = e;
+    }
+    block_expert[bx] = owner;
+  }
+  return n_valid;
+}
+
+// ---------------------------------------------------- expert MLP per pair --
+// h (length D) and expert_out (length H) of one (token, expert) pair, as fp32
+// values after the dtype rounding described above.
+int oracle_expert_pair(int dt, const void* x, const void* wg, const void* wu,
+                       const void* wd, int token, int expert, int H, int D,
+                       float* h_out, float* eo_out) {
+  if (!dtype_ok(dt) || H <= 0 || D <= 0) return -1;
+  std::vector<float> xrow(H);
+  for (int k = 0; k < H; ++k) xrow[k] = load_elem(dt, x, static_cast<int64_t>(token) * H + k);
+  expert_pair(dt, xrow.data(), wg, wu, wd, expert, H, D, h_out, eo_out);
+  return 0;
+}
+
+// ---------------------------------------------------------- full forward ---
+//   y[t, :] = sum over k ascending with ids[t,k] >= 0 of
+//             w[t,k] * expert_out(t, ids[t,k])[:]
+// accumulated in fp32 with fused multiply-add ([C] section 1: fp32
+// accumulator, K order kept, masked slots skipped; the routing weight is
+// applied once, here, as the reduce of [C] does).
+// tokens: optional list of n_tokens token indices to evaluate (NULL = all T
+// tokens, n_tokens must then equal T). y is [n_tokens, H] fp32. h_pairs
+// ([n_tokens*K, D]) and eo_pairs ([n_tokens*K, H]) are optional per-slot
+// intermediates in the same (token, k) order; masked slots get zeros.
+// Parallel over tokens with OpenMP; each token's arithmetic is sequential,
+// so the result does not depend on the thread count.
+int oracle_moe_forward(int dt, const void* x, const void* wg, const void* wu,
+                       const void* wd, const int32_t* ids, const float* w, int T,
+                       int H, int D, int E, int K, const int32_t* tokens,
+                       int n_tokens, float* y, float* h_pairs, float* eo_pairs) {
+  if (!dtype_ok(dt) || T < 0 || H <= 0 || D <= 0 || E <= 0 || K <= 0) return -1;
+  if (!tokens && n_tokens != T) return -1;
+  for (int i = 0; i < n_tokens; ++i) {
+    const int t = tokens ? tokens[i] : i;
+    if (t < 0 || t >= T) return -1;
+    for (int k = 0; k < K; ++k) {
+      if (ids[static_cast<int64_t>(t) * K + k] >= E) return -1;
+    }
+  }
+#pragma omp parallel
+  {
+    std::vector<float> xrow(H), hbuf(D), eo(H), acc(H);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < n_tokens; ++i) {
+      const int t = tokens ? tokens[i] : i;
+      for (int c = 0; c < H; ++c) xrow[c] = load_elem(dt, x, static_cast<int64_t>(t) * H + c);
+      for (int c = 0; c < H; ++c) acc[c] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int64_t slot = static_cast<int64_t>(t) * K + k;
+        const int64_t out_slot = static_cast<int64_t>(i) * K + k;
+        const int e = ids[slot];
+        if (e < 0) {
+          if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = 0.0f;
+          if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = 0.0f;
+          continue;
+        }
+        expert_pair(dt, xrow.data(), wg, wu, wd, e, H, D, hbuf.data(), eo.data());
+        const float wk = w[slot];
+        for (int c = 0; c < H; ++c) acc[c] = std::fma(wk, eo[c], acc[c]);
+        if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = hbuf[j];
+        if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = eo[c];
+      }
+      for (int c = 0; c < H; ++c) y[static_cast<int64_t>(i) * H + c] = acc[c];
+    }
+  }
+  return 0;
+}
+
+// -------------------------------------------------------- weighted reduce --
+// moe_reduce_fused ([C] sections 1-2):
+//   y[t, :] = sum over k ascending with pos[t,k] >= 0 of w[t,k] * X[pos[t,k], :]
+// fp32 accumulation with fused multiply-add; w == NULL means all-ones
+// weights. X is [R, H] in dtype dt; y is [T, H] fp32. Rows named by masked
+// slots are never read. Returns -1 when a position is >= R.
+int oracle_reduce(int dt, const void* X, int64_t R, const int32_t* pos,
+                  const float* w, int T, int K, int H, float* y) {
+  if (!dtype_ok(dt) || T < 0 || K <= 0 || H <= 0 || R < 0) return -1;
+  const int64_t P = static_cast<int64_t>(T) * K;
+  for (int64_t s = 0; s < P; ++s) {
+    if (pos[s] >= R) return -1;
+  }
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    float* yt = y + static_cast<int64_t>(t) * H;
+    for (int c = 0; c < H; ++c) yt[c] = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const int64_t slot = static_cast<int64_t>(t) * K + k;
+      const int32_t p = pos[slot];
+      if (p < 0) continue;
+      const float wk = w ? w[slot] : 1.0f;
+      for (int c = 0; c < H; ++c) {
+        yt[c] = std::fma(wk, load_elem(dt, X, static_cast<int64_t>(p) * H + c), yt[c]);
+      }
+    }
+  }
+  return 0;
+}
+
+}  // extern "C"
