@@ -1,0 +1,201 @@
+/*
+ * moe_routed.h -- C ABI of libmoe_routed: the routed-expert MoE forward on
+ * AMD Instinct MI355X (gfx950, CDNA4), one GPU.
+ *
+ * The forward computes, for every token t with top-k expert ids e_k and
+ * routing weights w_k,
+ *
+ *     y[t] = sum_k w_k * Down_{e_k}( SiLU(Gate_{e_k} x_t) * Up_{e_k} x_t )
+ *
+ * in three steps, each a call of this library:
+ *   1. moe_dispatch         -- expert-sorted dispatch tables;
+ *   2. moe_expert_gate_up   -- grouped GEMM over the stacked gate/up weights
+ *                              with SiLU(gate)*up fused in the epilogue,
+ *      moe_expert_down      -- grouped GEMM over the stacked down weights;
+ *   3. moe_reduce_fused     -- top-k weighted fp32 reduce back to token order.
+ * moe_routed_forward runs step 2 and step 3 back to back.
+ *
+ * Sources (page title, section):
+ *   [A] "tilelang baseline" MoE walkthrough (devpress.csdn.net, tilelang-metax
+ *       race): section "forward" (sorting, counts, offsets, padded offsets,
+ *       block->expert table), sections "stage-1 gate+up" and "stage-2 down".
+ *   [B] TileLang tutorial ch.18 "End-to-end II", skeletons.py,
+ *       moe_routed_kernel: the dispatch contract (the kernel takes its
+ *       tables from the caller and recovers its rows from them).
+ *   [C] TileOPs-Metax PR #55 "moe_reduce_fused": section 1 (design),
+ *       section 2 (reference semantics and error cases).
+ *
+ * Conventions for every call:
+ *   - Every array argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates or frees memory and keeps no state other than
+ *     a thread-local error message.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream). Nothing synchronises with the host. A kernel fault surfaces at
+ *     the caller's next synchronisation.
+ *   - All argument validation happens on the host before any launch; a call
+ *     that returns an error has launched nothing. moe_last_error() then holds
+ *     a message naming the argument.
+ *   - Row-major layouts throughout. 16-bit tensors (fp16, bf16) hold IEEE
+ *     binary16 / bfloat16 bit patterns. Accumulation is fp32; 16-bit results
+ *     are rounded to nearest, ties to even.
+ *   - Sizes: T tokens, K = top_k slots per token, E experts, H = d_hidden,
+ *     D = d_expert, P = T*K routed pairs.
+ */
+#ifndef MOE_ROUTED_H
+#define MOE_ROUTED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or not divisible         */
+  MOE_ERR_DTYPE = 3,       /* a dtype code is not supported by this call      */
+  MOE_ERR_UNSUPPORTED = 4, /* e.g. block_m not in {16, 32, 64, 128, 256}      */
+  MOE_ERR_WORKSPACE = 5,   /* the caller's buffer is too small                */
+  MOE_ERR_HIP = 6          /* a launch failed (message from the HIP runtime)  */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2 } moe_dtype;
+
+/*
+ * Dispatch tables ([A] "forward" steps 2-5, [B] dispatch contract).
+ * moe_tables_bind() fills this struct with views into ONE caller-allocated
+ * device buffer; moe_dispatch() fills the buffer. For a sorted row i
+ * (0 <= i < n_valid, rows grouped by expert in ascending expert order and,
+ * inside a group, in ascending flat slot order p = t*K + k):
+ *   group_sizes[e]          rows routed to expert e                      [E]
+ *   group_offsets[e]        exclusive prefix sum of group_sizes          [E]
+ *   group_padded_offsets[e] 0 for e = 0, else
+ *                           padded[e-1] + ceil((group_sizes[e-1]+1)/block_m)*block_m
+ *                           (every expert owns >= 1 block; a group whose size
+ *                           is a multiple of block_m gets one extra block)   [E]
+ *   block_expert[b]         the last expert e with padded[e] <= b*block_m;
+ *                           blocks past the last group belong to E-1
+ *                           and hold no rows                       [num_blocks]
+ *   sorted_pair[i]          the flat slot p of sorted row i             [P]
+ *   sorted_token[i]         p / K                                        [P]
+ *   sorted_weight[i]        topk_weights[p] (fp32, copied bit-exactly)   [P]
+ *   token_topk_to_pos[p]    the sorted row of slot p, -1 if masked       [P]
+ *   topk_weights[p]         fp32 copy of the routing weights, token order [P]
+ *   status[0]               0, or 1 if an id >= E was seen (it is then
+ *                           treated as a masked slot)                    [1]
+ * Entries i >= n_valid of the sorted_* arrays are unspecified. A slot with a
+ * negative id is masked: it is not counted and never read. The scan scratch
+ * (chunk_counts, chunk_flags, pair_rank) is internal. moe_dispatch writes
+ * every table entry it defines on each call (no memset is needed, so the
+ * call may be captured into a HIP graph).
+ */
+typedef struct moe_tables {
+  int32_t T, K, E, block_m;
+  int32_t num_blocks; /* ceil(T*K / block_m) + E                          */
+  int32_t num_chunks; /* ceil(T*K / 1024): dispatch scan chunks            */
+  int32_t *group_sizes, *group_offsets, *group_padded_offsets;
+  int32_t *block_expert;
+  int32_t *sorted_pair, *sorted_token;
+  float *sorted_weight;
+  int32_t *token_topk_to_pos;
+  float *topk_weights;
+  int32_t *status;
+  int32_t *chunk_counts; /* [num_chunks * E] */
+  int32_t *chunk_flags;  /* [num_chunks]     */
+  int32_t *pair_rank;    /* [P]              */
+} moe_tables;
+
+/* Human-readable name of a status code; never NULL. */
+const char* moe_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Bytes of device memory the tables need (0 if the sizes are invalid:
+ * T >= 1, 1 <= K <= 64, 1 <= E <= 1024, block_m in {16,32,64,128,256},
+ * T*K < 2^31). */
+size_t moe_tables_bytes(int T, int K, int E, int block_m);
+
+/* Carve `tables` out of `buffer` (device memory of at least `bytes` bytes,
+ * 256-byte aligned). Host-only: touches no device memory.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (block_m),
+ * MOE_ERR_WORKSPACE (bytes < moe_tables_bytes). */
+moe_status moe_tables_bind(moe_tables* tables, void* buffer, size_t bytes, int T, int K,
+                           int E, int block_m);
+
+/* Step 1: build the dispatch tables from the router output ([A] "forward";
+ * [B] dispatch contract; the inverse map token_topk_to_pos is the input of
+ * [C]'s reduce).
+ *   topk_ids      int32 [T, K]; values in [0, E), or negative = masked slot.
+ *   topk_weights  fp32 [T, K]; NULL means every weight is 1.
+ * Deterministic: the permutation is stable in p (a counting sort built from
+ * wavefront ballots and prefix scans; no atomics decide any position).
+ * Errors: MOE_ERR_NULL (tables, topk_ids, or unbound tables), MOE_ERR_HIP. */
+moe_status moe_dispatch(const int32_t* topk_ids, const float* topk_weights,
+                        moe_tables* tables, void* stream);
+
+/* Step 2a: grouped gate/up GEMM with fused SiLU(gate)*up ([A] "stage-1
+ * gate+up"; [B] moe_routed_kernel, first kernel).
+ *   x       [T, H] dtype;  w_gate, w_up [E, D, H] dtype (stacked, one [D, H]
+ *           matrix per expert, so both GEMMs contract over contiguous rows).
+ *   h       [P, D] dtype output, row i = sorted row i:
+ *           h[i, j] = R( SiLU(g) * u ),  g = x[sorted_token[i]] . w_gate[e, j],
+ *           u = x[sorted_token[i]] . w_up[e, j], e the expert of row i,
+ *           SiLU(g) = g / (1 + exp(-g)), fp32 accumulation, R = rounding to
+ *           dtype. Rows >= n_valid are not written.
+ *   dtype   MOE_BF16 or MOE_F16.
+ * Requires H % 256 == 0 and D % 128 == 0.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP. */
+moe_status moe_expert_gate_up(const void* x, const void* w_gate, const void* w_up,
+                              const moe_tables* tables, int H, int D, int dtype, void* h,
+                              void* stream);
+
+/* Step 2b: grouped down GEMM ([A] "stage-2 down"; [B] moe_routed_kernel,
+ * second kernel), WITHOUT the routing weight (it is applied once, in the
+ * reduce, as [C] does):
+ *   h           [P, D] dtype (the output of moe_expert_gate_up);
+ *   w_down      [E, H, D] dtype;
+ *   expert_out  [P, H] dtype output: expert_out[i, c] = R( h[i] . w_down[e, c] ).
+ * Same requirements and errors as moe_expert_gate_up. */
+moe_status moe_expert_down(const void* h, const void* w_down, const moe_tables* tables, int H,
+                           int D, int dtype, void* expert_out, void* stream);
+
+/* Workspace of moe_routed_forward: h [P, D] at offset 0, then expert_out
+ * [P, H] at the next 256-byte boundary (both of dtype). 0 if invalid. */
+size_t moe_forward_workspace_bytes(int T, int K, int H, int D, int dtype);
+
+/* Byte offset of expert_out inside that workspace. */
+size_t moe_forward_workspace_expert_out_offset(int T, int K, int H, int D, int dtype);
+
+/* Steps 2-3: y [T, H] dtype = moe_reduce_fused(moe_expert_down(moe_expert_gate_up(x)),
+ * tables->token_topk_to_pos, tables->topk_weights). The intermediates stay
+ * in `workspace` (layout above) and may be read back by the caller.
+ * Errors: as the three steps, plus MOE_ERR_WORKSPACE. */
+moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_up,
+                              const void* w_down, const moe_tables* tables, int H, int D,
+                              int dtype, void* workspace, size_t workspace_bytes, void* y,
+                              void* stream);
+
+/* Step 3: top-k weighted reduce back to token order ([C] sections 1-2):
+ *   y[t, :] = R_out( sum over k = 0..K-1 ascending with pos[t,k] >= 0 of
+ *                    w[t,k] * expert_out[pos[t,k], :] )
+ * accumulated in fp32 with fused multiply-add in k order, cast once at the
+ * end. Slots with pos < 0 are neither read nor accumulated; a token whose
+ * slots are all masked gets zeros.
+ *   expert_out         [rows, H] of in_dtype;
+ *   token_topk_to_pos  int32 [T, K], each value < rows;
+ *   topk_weights       fp32 [T, K], or NULL for all-ones weights;
+ *   y                  [T, H] of out_dtype (any of MOE_F16, MOE_BF16, MOE_F32).
+ * Requires H % 256 == 0 ([C] section 2 lists H % 256 != 0 as an error case).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP. */
+moe_status moe_reduce_fused(const void* expert_out, int64_t rows,
+                            const int32_t* token_topk_to_pos, const float* topk_weights, int T,
+                            int K, int H, int in_dtype, int out_dtype, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTED_H */

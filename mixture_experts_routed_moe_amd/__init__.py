@@ -1,0 +1,233 @@
+"""Routed-expert MoE forward on AMD Instinct MI355X (gfx950) -- Python binding.
+
+Argument marshalling only: every step runs in the HIP kernels of
+libmoe_routed.so, called through its C ABI (include/moe_routed.h). PyTorch
+supplies device memory and the current stream; the binding checks dtypes,
+shapes, devices and contiguity (the C ABI sees raw pointers only) and raises
+MoeError with the library's status code on any failure.
+
+    tables = moe_dispatch(topk_ids, topk_weights, num_experts)      # step 1
+    y = moe_routed_forward(x, w_gate, w_up, w_down, tables)         # steps 2-3
+    y = moe_reduce_fused(expert_out, token_topk_to_pos, topk_weights)  # step 3 alone
+"""
+import ctypes
+import math
+
+import torch
+
+from ._lib import (MOE_BF16, MOE_ERR_DTYPE, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_F16, MOE_F32,
+                   MoeError, MoeTablesStruct, check, lib)
+
+__all__ = ["MoeError", "MoeTables", "default_block_m", "moe_dispatch", "moe_expert_gate_up",
+           "moe_expert_down", "moe_routed_forward", "moe_reduce_fused", "forward_workspace"]
+
+_DTYPE_CODE = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
+
+_TABLE_FIELDS = {
+    "group_sizes": ("E", torch.int32), "group_offsets": ("E", torch.int32),
+    "group_padded_offsets": ("E", torch.int32), "block_expert": ("num_blocks", torch.int32),
+    "sorted_pair": ("P", torch.int32), "sorted_token": ("P", torch.int32),
+    "sorted_weight": ("P", torch.float32), "token_topk_to_pos": ("P", torch.int32),
+    "topk_weights": ("P", torch.float32), "status": ("one", torch.int32),
+}
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _require(cond, status, msg):
+    if not cond:
+        raise MoeError(status, msg)
+
+
+def _check_tensor(t, name, dtype=None, ndim=None, device=None):
+    _require(t is not None, MOE_ERR_NULL, "%s must not be None" % name)
+    _require(t.is_cuda, MOE_ERR_SHAPE, "%s must be a GPU tensor" % name)
+    if device is not None:
+        _require(t.device == device, MOE_ERR_SHAPE, "%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None:
+        _require(t.dtype == dtype, MOE_ERR_DTYPE, "%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if ndim is not None:
+        _require(t.dim() == ndim, MOE_ERR_SHAPE, "%s must be %d-D (got shape %s)" % (name, ndim, tuple(t.shape)))
+    _require(t.is_contiguous(), MOE_ERR_SHAPE, "%s must be contiguous" % name)
+
+
+def default_block_m(T, K, E):
+    """Row-block size of the tables: the power of two >= twice the mean rows
+    per expert, clamped to [16, 128], so a typical expert fits in one block."""
+    avg = max(1.0, T * K / E)
+    bm = 1 << max(0, math.ceil(math.log2(2 * avg)))
+    return int(min(128, max(16, bm)))
+
+
+class MoeTables:
+    """Dispatch tables in one device buffer (struct moe_tables of the C ABI)."""
+
+    def __init__(self, T, K, E, block_m, device):
+        nbytes = lib().moe_tables_bytes(T, K, E, block_m)
+        if nbytes == 0:
+            # Let the library name the bad argument.
+            s = MoeTablesStruct()
+            check(lib().moe_tables_bind(ctypes.byref(s), ctypes.c_void_p(256), 0, T, K, E, block_m))
+        self.T, self.K, self.E, self.block_m = T, K, E, block_m
+        self.device = torch.device(device)
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.struct = MoeTablesStruct()
+        check(lib().moe_tables_bind(ctypes.byref(self.struct), _ptr(self.buffer), nbytes,
+                                    T, K, E, block_m))
+        self.num_blocks = self.struct.num_blocks
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+    def tensor(self, name):
+        """A torch view of one table (see the header for its meaning)."""
+        count, dtype = _TABLE_FIELDS[name]
+        n = {"E": self.E, "num_blocks": self.num_blocks, "P": self.T * self.K, "one": 1}[count]
+        off = getattr(self.struct, name) - self.buffer.data_ptr()
+        raw = self.buffer[off:off + 4 * n]
+        return raw.view(dtype)
+
+    def __getattr__(self, name):
+        if name in _TABLE_FIELDS:
+            return self.tensor(name)
+        raise AttributeError(name)
+
+
+def moe_dispatch(topk_ids, topk_weights, num_experts, block_m=None, tables=None):
+    """Step 1: expert-sorted dispatch tables from top-k ids [T, K] (int32,
+    negative = masked slot) and weights [T, K] (float32, or None = ones)."""
+    _check_tensor(topk_ids, "topk_ids", torch.int32, 2)
+    T, K = topk_ids.shape
+    if topk_weights is not None:
+        _check_tensor(topk_weights, "topk_weights", torch.float32, 2, topk_ids.device)
+        _require(tuple(topk_weights.shape) == (T, K), MOE_ERR_SHAPE,
+                 "topk_weights shape %s != topk_ids shape %s" % (tuple(topk_weights.shape), (T, K)))
+    if block_m is None:
+        block_m = default_block_m(T, K, num_experts)
+    if tables is None:
+        tables = MoeTables(T, K, num_experts, block_m, topk_ids.device)
+    else:
+        _require((tables.T, tables.K, tables.E, tables.block_m) == (T, K, num_experts, block_m),
+                 MOE_ERR_SHAPE, "tables were bound for other sizes")
+    check(lib().moe_dispatch(_ptr(topk_ids), _ptr(topk_weights), tables.ref,
+                             _stream(topk_ids.device)))
+    return tables
+
+
+def _expert_shapes(x_or_h, w_a, w_b, w_down, tables, gate_up):
+    dt = x_or_h.dtype
+    _require(dt in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "expert GEMMs take float16 or bfloat16 (got %s)" % dt)
+    E = tables.E
+    if gate_up:
+        T, H = x_or_h.shape
+        _require(T == tables.T, MOE_ERR_SHAPE, "x has %d tokens, tables %d" % (T, tables.T))
+        _require(w_a.dim() == 3 and w_a.shape[0] == E and w_a.shape[2] == H, MOE_ERR_SHAPE,
+                 "w_gate must be [E=%d, D, H=%d] (got %s)" % (E, H, tuple(w_a.shape)))
+        D = w_a.shape[1]
+        _require(tuple(w_b.shape) == (E, D, H), MOE_ERR_SHAPE,
+                 "w_up must be [%d, %d, %d] (got %s)" % (E, D, H, tuple(w_b.shape)))
+        if w_down is not None:
+            _require(tuple(w_down.shape) == (E, H, D), MOE_ERR_SHAPE,
+                     "w_down must be [%d, %d, %d] (got %s)" % (E, H, D, tuple(w_down.shape)))
+        return H, D
+    P, D = x_or_h.shape
+    _require(P == tables.T * tables.K, MOE_ERR_SHAPE, "h must have T*K rows")
+    _require(w_a.dim() == 3 and w_a.shape[0] == E and w_a.shape[2] == D, MOE_ERR_SHAPE,
+             "w_down must be [E=%d, H, D=%d] (got %s)" % (E, D, tuple(w_a.shape)))
+    return w_a.shape[1], D
+
+
+def moe_expert_gate_up(x, w_gate, w_up, tables, h=None):
+    """Step 2a: h [T*K, D] = SiLU(x W_gate^T) * (x W_up^T) per sorted row."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    for n, w in (("w_gate", w_gate), ("w_up", w_up)):
+        _check_tensor(w, n, x.dtype, 3, tables.device)
+    H, D = _expert_shapes(x, w_gate, w_up, None, tables, True)
+    if h is None:
+        h = torch.empty(tables.T * tables.K, D, dtype=x.dtype, device=x.device)
+    _check_tensor(h, "h", x.dtype, 2, tables.device)
+    check(lib().moe_expert_gate_up(_ptr(x), _ptr(w_gate), _ptr(w_up), tables.ref, H, D,
+                                   _DTYPE_CODE[x.dtype], _ptr(h), _stream(x.device)))
+    return h
+
+
+def moe_expert_down(h, w_down, tables, expert_out=None):
+    """Step 2b: expert_out [T*K, H] = h W_down^T per sorted row (unweighted)."""
+    _check_tensor(h, "h", None, 2, tables.device)
+    _check_tensor(w_down, "w_down", h.dtype, 3, tables.device)
+    H, D = _expert_shapes(h, w_down, None, None, tables, False)
+    if expert_out is None:
+        expert_out = torch.empty(tables.T * tables.K, H, dtype=h.dtype, device=h.device)
+    _check_tensor(expert_out, "expert_out", h.dtype, 2, tables.device)
+    check(lib().moe_expert_down(_ptr(h), _ptr(w_down), tables.ref, H, D, _DTYPE_CODE[h.dtype],
+                                _ptr(expert_out), _stream(h.device)))
+    return expert_out
+
+
+def forward_workspace(tables, H, D, dtype):
+    """A workspace for moe_routed_forward and views of its h / expert_out."""
+    code = _DTYPE_CODE[dtype]
+    nbytes = lib().moe_forward_workspace_bytes(tables.T, tables.K, H, D, code)
+    _require(nbytes > 0, MOE_ERR_SHAPE, "invalid workspace sizes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=tables.device)
+    off = lib().moe_forward_workspace_expert_out_offset(tables.T, tables.K, H, D, code)
+    P = tables.T * tables.K
+    esz = torch.empty((), dtype=dtype).element_size()
+    h = ws[:P * D * esz].view(dtype).view(P, D)
+    eo = ws[off:off + P * H * esz].view(dtype).view(P, H)
+    return ws, h, eo
+
+
+def moe_routed_forward(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
+    """Steps 2-3: y [T, H] of x.dtype. `workspace` from forward_workspace()
+    (allocated here when None)."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_tensor(w, n, x.dtype, 3, tables.device)
+    H, D = _expert_shapes(x, w_gate, w_up, w_down, tables, True)
+    if workspace is None:
+        workspace = forward_workspace(tables, H, D, x.dtype)[0]
+    _check_tensor(workspace, "workspace", torch.uint8, 1, tables.device)
+    if y is None:
+        y = torch.empty(tables.T, H, dtype=x.dtype, device=x.device)
+    _check_tensor(y, "y", x.dtype, 2, tables.device)
+    _require(tuple(y.shape) == (tables.T, H), MOE_ERR_SHAPE, "y must be [T, H]")
+    check(lib().moe_routed_forward(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), tables.ref,
+                                   H, D, _DTYPE_CODE[x.dtype], _ptr(workspace),
+                                   workspace.numel(), _ptr(y), _stream(x.device)))
+    return y
+
+
+def moe_reduce_fused(expert_out, token_topk_to_pos, topk_weights=None, out_dtype=None, y=None):
+    """Step 3: y[t] = sum_k w[t,k] * expert_out[pos[t,k]] over pos >= 0, fp32
+    accumulation, one cast to out_dtype (default: expert_out's dtype)."""
+    _check_tensor(expert_out, "expert_out", None, 2)
+    _require(expert_out.dtype in _DTYPE_CODE, MOE_ERR_DTYPE,
+             "expert_out dtype %s not supported" % expert_out.dtype)
+    dev = expert_out.device
+    _check_tensor(token_topk_to_pos, "token_topk_to_pos", torch.int32, 2, dev)
+    T, K = token_topk_to_pos.shape
+    R, H = expert_out.shape
+    if topk_weights is not None:
+        _check_tensor(topk_weights, "topk_weights", torch.float32, 2, dev)
+        _require(tuple(topk_weights.shape) == (T, K), MOE_ERR_SHAPE,
+                 "topk_weights shape %s != token_topk_to_pos shape %s"
+                 % (tuple(topk_weights.shape), (T, K)))
+    out_dtype = expert_out.dtype if out_dtype is None else out_dtype
+    _require(out_dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "out_dtype %s not supported" % out_dtype)
+    if y is None:
+        y = torch.empty(T, H, dtype=out_dtype, device=dev)
+    _check_tensor(y, "y", out_dtype, 2, dev)
+    _require(tuple(y.shape) == (T, H), MOE_ERR_SHAPE, "y must be [T, H]")
+    check(lib().moe_reduce_fused(_ptr(expert_out), R, _ptr(token_topk_to_pos), _ptr(topk_weights),
+                                 T, K, H, _DTYPE_CODE[expert_out.dtype], _DTYPE_CODE[out_dtype],
+                                 _ptr(y), _stream(dev)))
+    return y

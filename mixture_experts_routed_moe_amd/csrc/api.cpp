@@ -1,0 +1,280 @@
+// C-ABI layer of libmoe_routed: argument validation, table/workspace layout
+// and launches. Every check runs on the host before anything is launched.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "launch.hpp"
+#include "moe_routed.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+constexpr int kDispatchChunk = 1024;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+bool block_m_ok(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+bool is_16bit(int dt) { return dt == MOE_F16 || dt == MOE_BF16; }
+
+size_t dtype_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+moe_status check_table_sizes(int T, int K, int E, int block_m) {
+  if (T < 1) return fail(MOE_ERR_SHAPE, "T must be >= 1 (got %d)", T);
+  if (K < 1 || K > 64) return fail(MOE_ERR_SHAPE, "K must be in [1, 64] (got %d)", K);
+  if (E < 1 || E > 1024) return fail(MOE_ERR_SHAPE, "E must be in [1, 1024] (got %d)", E);
+  if (!block_m_ok(block_m)) {
+    return fail(MOE_ERR_UNSUPPORTED, "block_m must be one of 16, 32, 64, 128, 256 (got %d)",
+                block_m);
+  }
+  const int64_t P = static_cast<int64_t>(T) * K;
+  const int64_t nb = (P + block_m - 1) / block_m + E;
+  if (P >= (int64_t{1} << 31) || nb * block_m >= (int64_t{1} << 31)) {
+    return fail(MOE_ERR_SHAPE, "T*K too large (%lld pairs)", static_cast<long long>(P));
+  }
+  return MOE_OK;
+}
+
+struct TableLayout {
+  size_t group_sizes, group_offsets, group_padded_offsets, block_expert, sorted_pair,
+      sorted_token, sorted_weight, token_topk_to_pos, topk_weights, status, chunk_counts,
+      chunk_flags, pair_rank, total;
+  int num_blocks, num_chunks;
+};
+
+TableLayout table_layout(int T, int K, int E, int block_m) {
+  TableLayout L{};
+  const size_t P = static_cast<size_t>(T) * K;
+  L.num_blocks = static_cast<int>((P + block_m - 1) / block_m + E);
+  L.num_chunks = static_cast<int>((P + kDispatchChunk - 1) / kDispatchChunk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.group_sizes = take(4 * static_cast<size_t>(E));
+  L.group_offsets = take(4 * static_cast<size_t>(E));
+  L.group_padded_offsets = take(4 * static_cast<size_t>(E));
+  L.block_expert = take(4 * static_cast<size_t>(L.num_blocks));
+  L.sorted_pair = take(4 * P);
+  L.sorted_token = take(4 * P);
+  L.sorted_weight = take(4 * P);
+  L.token_topk_to_pos = take(4 * P);
+  L.topk_weights = take(4 * P);
+  L.status = take(4);
+  L.chunk_counts = take(4 * static_cast<size_t>(L.num_chunks) * E);
+  L.chunk_flags = take(4 * static_cast<size_t>(L.num_chunks));
+  L.pair_rank = take(4 * P);
+  L.total = off;
+  return L;
+}
+
+bool tables_bound(const moe_tables* t) {
+  return t && t->group_sizes && t->group_offsets && t->group_padded_offsets &&
+         t->block_expert && t->sorted_pair && t->sorted_token && t->sorted_weight &&
+         t->token_topk_to_pos && t->topk_weights && t->status && t->chunk_counts &&
+         t->chunk_flags && t->pair_rank;
+}
+
+moe_status hip_status(hipError_t err, const char* what) {
+  if (err != hipSuccess) {
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+  }
+  return ok();
+}
+
+moe_status check_expert_shapes(const moe_tables* t, int H, int D, int dtype) {
+  if (!tables_bound(t)) return fail(MOE_ERR_NULL, "tables are NULL or not bound");
+  if (!is_16bit(dtype)) {
+    return fail(MOE_ERR_DTYPE, "expert GEMMs take MOE_F16 or MOE_BF16 (got dtype %d)", dtype);
+  }
+  if (H <= 0 || H % 256 != 0) return fail(MOE_ERR_SHAPE, "H must be a positive multiple of 256 (got %d)", H);
+  if (D <= 0 || D % 128 != 0) return fail(MOE_ERR_SHAPE, "D must be a positive multiple of 128 (got %d)", D);
+  return MOE_OK;
+}
+
+size_t ws_h_bytes(int T, int K, int D, int dtype) {
+  return static_cast<size_t>(T) * K * D * dtype_bytes(dtype);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_tables_bytes(int T, int K, int E, int block_m) {
+  if (check_table_sizes(T, K, E, block_m) != MOE_OK) return 0;
+  return table_layout(T, K, E, block_m).total;
+}
+
+moe_status moe_tables_bind(moe_tables* tables, void* buffer, size_t bytes, int T, int K, int E,
+                           int block_m) {
+  if (!tables || !buffer) return fail(MOE_ERR_NULL, "tables and buffer must not be NULL");
+  const moe_status s = check_table_sizes(T, K, E, block_m);
+  if (s != MOE_OK) return s;
+  if (reinterpret_cast<uintptr_t>(buffer) % kAlign != 0) {
+    return fail(MOE_ERR_WORKSPACE, "table buffer must be 256-byte aligned");
+  }
+  const TableLayout L = table_layout(T, K, E, block_m);
+  if (bytes < L.total) {
+    return fail(MOE_ERR_WORKSPACE, "table buffer has %zu bytes, needs %zu", bytes, L.total);
+  }
+  char* b = static_cast<char*>(buffer);
+  tables->T = T;
+  tables->K = K;
+  tables->E = E;
+  tables->block_m = block_m;
+  tables->num_blocks = L.num_blocks;
+  tables->num_chunks = L.num_chunks;
+  tables->group_sizes = reinterpret_cast<int32_t*>(b + L.group_sizes);
+  tables->group_offsets = reinterpret_cast<int32_t*>(b + L.group_offsets);
+  tables->group_padded_offsets = reinterpret_cast<int32_t*>(b + L.group_padded_offsets);
+  tables->block_expert = reinterpret_cast<int32_t*>(b + L.block_expert);
+  tables->sorted_pair = reinterpret_cast<int32_t*>(b + L.sorted_pair);
+  tables->sorted_token = reinterpret_cast<int32_t*>(b + L.sorted_token);
+  tables->sorted_weight = reinterpret_cast<float*>(b + L.sorted_weight);
+  tables->token_topk_to_pos = reinterpret_cast<int32_t*>(b + L.token_topk_to_pos);
+  tables->topk_weights = reinterpret_cast<float*>(b + L.topk_weights);
+  tables->status = reinterpret_cast<int32_t*>(b + L.status);
+  tables->chunk_counts = reinterpret_cast<int32_t*>(b + L.chunk_counts);
+  tables->chunk_flags = reinterpret_cast<int32_t*>(b + L.chunk_flags);
+  tables->pair_rank = reinterpret_cast<int32_t*>(b + L.pair_rank);
+  return ok();
+}
+
+moe_status moe_dispatch(const int32_t* topk_ids, const float* topk_weights, moe_tables* tables,
+                        void* stream) {
+  if (!topk_ids) return fail(MOE_ERR_NULL, "topk_ids must not be NULL");
+  if (!tables_bound(tables)) return fail(MOE_ERR_NULL, "tables are NULL or not bound");
+  const moe_status s = check_table_sizes(tables->T, tables->K, tables->E, tables->block_m);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_dispatch(topk_ids, topk_weights, *tables,
+                                         static_cast<hipStream_t>(stream)),
+                    "moe_dispatch launch");
+}
+
+moe_status moe_expert_gate_up(const void* x, const void* w_gate, const void* w_up,
+                              const moe_tables* tables, int H, int D, int dtype, void* h,
+                              void* stream) {
+  if (!x || !w_gate || !w_up || !h) return fail(MOE_ERR_NULL, "x, w_gate, w_up and h must not be NULL");
+  moe_status s = check_expert_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  moe::GemmProblem p{x, w_gate, w_up, h, D, H, dtype};
+  return hip_status(moe::launch_gate_up(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_gate_up launch");
+}
+
+moe_status moe_expert_down(const void* h, const void* w_down, const moe_tables* tables, int H,
+                           int D, int dtype, void* expert_out, void* stream) {
+  if (!h || !w_down || !expert_out) return fail(MOE_ERR_NULL, "h, w_down and expert_out must not be NULL");
+  moe_status s = check_expert_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  moe::GemmProblem p{h, w_down, nullptr, expert_out, H, D, dtype};
+  return hip_status(moe::launch_down(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_down launch");
+}
+
+size_t moe_forward_workspace_expert_out_offset(int T, int K, int H, int D, int dtype) {
+  if (T < 1 || K < 1 || H <= 0 || D <= 0 || !is_16bit(dtype)) return 0;
+  return align_up(ws_h_bytes(T, K, D, dtype));
+}
+
+size_t moe_forward_workspace_bytes(int T, int K, int H, int D, int dtype) {
+  const size_t off = moe_forward_workspace_expert_out_offset(T, K, H, D, dtype);
+  if (off == 0) return 0;
+  return off + align_up(static_cast<size_t>(T) * K * H * dtype_bytes(dtype));
+}
+
+moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_up,
+                              const void* w_down, const moe_tables* tables, int H, int D,
+                              int dtype, void* workspace, size_t workspace_bytes, void* y,
+                              void* stream) {
+  if (!x || !w_gate || !w_up || !w_down || !workspace || !y) {
+    return fail(MOE_ERR_NULL, "x, w_gate, w_up, w_down, workspace and y must not be NULL");
+  }
+  moe_status s = check_expert_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  const size_t need = moe_forward_workspace_bytes(tables->T, tables->K, H, D, dtype);
+  if (workspace_bytes < need) {
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) {
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  char* ws = static_cast<char*>(workspace);
+  void* hbuf = ws;
+  void* eo = ws + moe_forward_workspace_expert_out_offset(tables->T, tables->K, H, D, dtype);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe::GemmProblem up{x, w_gate, w_up, hbuf, D, H, dtype};
+  hipError_t err = moe::launch_gate_up(up, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward gate/up launch");
+  moe::GemmProblem down{hbuf, w_down, nullptr, eo, H, D, dtype};
+  err = moe::launch_down(down, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward down launch");
+  const int64_t P = static_cast<int64_t>(tables->T) * tables->K;
+  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, tables->T,
+                           tables->K, H, dtype, dtype, y, st);
+  return hip_status(err, "moe_routed_forward reduce launch");
+}
+
+moe_status moe_reduce_fused(const void* expert_out, int64_t rows,
+                            const int32_t* token_topk_to_pos, const float* topk_weights, int T,
+                            int K, int H, int in_dtype, int out_dtype, void* y, void* stream) {
+  if (!expert_out || !token_topk_to_pos || !y) {
+    return fail(MOE_ERR_NULL, "expert_out, token_topk_to_pos and y must not be NULL");
+  }
+  if (rows < 0) return fail(MOE_ERR_SHAPE, "rows must be >= 0");
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T must be >= 0 (got %d)", T);
+  if (K < 1 || K > 64) return fail(MOE_ERR_SHAPE, "K must be in [1, 64] (got %d)", K);
+  if (H <= 0 || H % 256 != 0) {
+    return fail(MOE_ERR_SHAPE, "H must be a positive multiple of 256 (got %d)", H);
+  }
+  if (in_dtype < MOE_F16 || in_dtype > MOE_F32 || out_dtype < MOE_F16 || out_dtype > MOE_F32) {
+    return fail(MOE_ERR_DTYPE, "dtype codes must be MOE_F16, MOE_BF16 or MOE_F32");
+  }
+  if (static_cast<int64_t>(T) * (H / 256) > 0xffffffffLL) {
+    return fail(MOE_ERR_SHAPE, "T * H too large for one launch");
+  }
+  return hip_status(moe::launch_reduce(expert_out, rows, token_topk_to_pos, topk_weights, T, K, H,
+                                       in_dtype, out_dtype, y, static_cast<hipStream_t>(stream)),
+                    "moe_reduce_fused launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Host-side launchers of the HIP kernels (internal to libmoe_routed).
+// Arguments have been validated by the C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_routed.h"
+
+namespace moe {
+
+hipError_t launch_dispatch(const int32_t* topk_ids, const float* topk_weights,
+                           const moe_tables& t, hipStream_t stream);
+
+struct GemmProblem {
+  const void* a;         // gate/up: x [T, Kd]; down: h [P, Kd]
+  const void* b0;        // gate/up: W_gate [E, N, Kd]; down: W_down [E, N, Kd]
+  const void* b1;        // gate/up: W_up; down: unused
+  void* c;               // gate/up: h [P, N]; down: expert_out [P, N]
+  int n;                 // output columns (D for gate/up, H for down)
+  int kd;                // reduction length (H for gate/up, D for down)
+  int dtype;             // kF16 / kBF16
+};
+
+hipError_t launch_gate_up(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_down(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+
+hipError_t launch_reduce(const void* x, int64_t rows, const int32_t* pos, const float* w, int T,
+                         int K, int H, int in_dtype, int out_dtype, void* y, hipStream_t stream);
+
+}  // namespace moe
