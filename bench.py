@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE forward on one MI355X.
+
+One step = one pass of the whole hot path on one batch of synthetic input:
+  moe_dispatch -> moe_expert_gate_up (SiLU*up fused) -> moe_expert_down
+  -> moe_reduce_fused,
+exactly the kernels moe_routed_forward launches after the dispatch, called
+stage by stage so that HIP events (recorded on the stream the kernels run
+on) time every kernel inside the timed region.
+
+Workload (the metric's T = 512 case): the DeepSeek-shaped decode layer,
+T=512, d_hidden=7168, d_expert=2048, E=256 routed experts, top-8, bf16,
+seeded synthetic x / weights / router (no dataset, random-init weights).
+The same line also carries the metric's T = 4096 case (the prefill layer
+of the same shapes) under "t4096", and the CPU oracle timed on a bounded
+sample of the decode workload under "cpu_baseline".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "pmc_grouped_gemm_gate_up_deepseek_decode.md")
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", f)
+                for f in ("grouped_gemm.hip", "common.hpp")]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="index into synthetic.CONFIGS for the main line (default 2: decode T=512)")
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--no-t4096", action="store_true", help="skip the T=4096 prefill case")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=128,
+                    help="tokens of the decode workload the oracle runs for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def gemm_source_sha():
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter
+    summary, or None if it is missing or was taken on other kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != gemm_source_sha():
+        return None
+    return float(val.group(1))
+
+
+def workload_numbers(d, tables_sizes):
+    """Algorithmic FLOPs and bytes of one step, per kernel (units in the
+    design notes): weights of the experts that receive rows once, x read
+    once, h / expert_out written and read once, y written once."""
+    T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
+    b = d["x"].element_size()
+    n_valid = int(tables_sizes.sum())
+    e_active = int((tables_sizes > 0).sum())
+    P = T * K
+    gate_up_bytes = e_active * 2 * D * H * b + T * H * b + n_valid * D * b
+    down_bytes = e_active * H * D * b + n_valid * D * b + n_valid * H * b
+    reduce_bytes = n_valid * H * b + T * H * b + P * 8
+    dispatch_bytes = P * 8 + n_valid * 12 + P * 8 + 12 * E
+    flops_gate_up = 4 * n_valid * H * D
+    flops_down = 2 * n_valid * H * D
+    b_min = e_active * 3 * H * D * b + 2 * T * H * b + P * 8
+    return dict(n_valid=n_valid, e_active=e_active, gate_up_bytes=gate_up_bytes,
+                down_bytes=down_bytes, reduce_bytes=reduce_bytes, dispatch_bytes=dispatch_bytes,
+                flops_gate_up=flops_gate_up, flops_down=flops_down,
+                flops=flops_gate_up + flops_down, b_min=b_min)
+
+
+def time_workload(cfg, steps, warmup, block_m, dev):
+    import torch
+
+    import mixture_experts_routed_moe_amd as mr
+    import synthetic as S
+
+    t_gen = time.time()
+    d = S.make_moe_inputs(cfg, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+    T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
+    block_m = block_m or mr.default_block_m(T, K, E)
+    ids, w = d["topk_ids"], d["topk_weights"]
+    x, wg, wu, wd = d["x"], d["w_gate"], d["w_up"], d["w_down"]
+    tables = mr.MoeTables(T, K, E, block_m, dev)
+    ws, h, eo = mr.forward_workspace(tables, H, D, x.dtype)
+    y = torch.empty(T, H, dtype=x.dtype, device=dev)
+    pos = tables.token_topk_to_pos.view(T, K)
+    wt = tables.topk_weights.view(T, K)
+
+    def step(ev):
+        ev[0].record()
+        mr.moe_dispatch(ids, w, E, block_m=block_m, tables=tables)
+        ev[1].record()
+        mr.moe_expert_gate_up(x, wg, wu, tables, h=h)
+        ev[2].record()
+        mr.moe_expert_down(h, wd, tables, expert_out=eo)
+        ev[3].record()
+        mr.moe_reduce_fused(eo, pos, wt, y=y)
+        ev[4].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for _ in range(warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    events = [mk() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    names = ["dispatch", "gate_up", "down", "reduce"]
+    per = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps
+           for j, n in enumerate(names)}
+    span = sum(ev[0].elapsed_time(ev[4]) for ev in events) / steps
+    sizes = tables.group_sizes.cpu()
+    nums = workload_numbers(d, sizes)
+    return dict(d=d, tables=tables, block_m=block_m, wall_ms=wall_ms, event_ms=span,
+                kernel_ms=per, nums=nums, gen_s=t_gen)
+
+
+def summarize(r):
+    nums, per = r["nums"], r["kernel_ms"]
+    ms = r["wall_ms"]
+    gbs = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
+    kernels = {}
+    for n, key in (("dispatch", "dispatch_bytes"), ("gate_up", "gate_up_bytes"),
+                   ("down", "down_bytes"), ("reduce", "reduce_bytes")):
+        kernels[n] = {"ms": round(per[n], 4), "algo_bytes": nums[key],
+                      "GB_s": round(gbs(nums[key], per[n]), 1),
+                      "hbm_frac": round(gbs(nums[key], per[n]) / HBM_PEAK_GBS, 4)}
+    for n, key in (("gate_up", "flops_gate_up"), ("down", "flops_down")):
+        kernels[n]["TFLOP_s"] = round(nums[key] / (per[n] * 1e-3) / 1e12, 2)
+    tflops = nums["flops"] / (ms * 1e-3) / 1e12
+    hbm = gbs(nums["b_min"], ms)
+    t_roof_ms = max(nums["b_min"] / (HBM_PEAK_GBS * 1e9), nums["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    return dict(ms_per_layer=round(ms, 4), event_ms_per_layer=round(r["event_ms"], 4),
+                TFLOP_s=round(tflops, 2), HBM_GB_s=round(hbm, 1),
+                hbm_frac=round(hbm / HBM_PEAK_GBS, 4),
+                mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                roofline_frac=round(t_roof_ms / ms, 4), roofline_ms=round(t_roof_ms, 4),
+                flops=nums["flops"], b_min_bytes=nums["b_min"], n_valid=nums["n_valid"],
+                active_experts=nums["e_active"], block_m=r["block_m"], kernels=kernels)
+
+
+def cpu_baseline(r, n_tokens):
+    """The oracle (as it stands) on the first n_tokens tokens of the workload,
+    plus its dispatch of the whole batch; time scaled to the whole layer."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    d = r["d"]
+    T, K, E = d["T"], d["K"], d["E"]
+    n_tokens = min(n_tokens, T)
+    tokens = np.arange(n_tokens, dtype=np.int32)
+    ids = d["topk_ids"].cpu().numpy()
+    w = d["topk_weights"].cpu().numpy()
+    sub = ids[:n_tokens]
+    used = np.unique(sub[sub >= 0])
+    remap = np.full(E, -1, np.int32)
+    remap[used] = np.arange(used.size, dtype=np.int32)
+    sub_ids = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
+    sel = torch.from_numpy(used).long().to(d["x"].device)
+    bits = lambda t: t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    xs, gs, us, ds = (bits(d["x"][:n_tokens]), bits(d["w_gate"][sel]), bits(d["w_up"][sel]),
+                      bits(d["w_down"][sel]))
+    t0 = time.perf_counter()
+    oracle.dispatch(ids, w, E, r["block_m"])
+    t_disp = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.moe_forward(oracle.BF16, xs, gs, us, ds, sub_ids, w[:n_tokens], tokens=tokens)
+    t_fwd = time.perf_counter() - t0
+    ms = (t_disp + t_fwd * T / n_tokens) * 1e3
+    return {"value": round(ms, 1), "unit": "ms/layer", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "oracle forward on %d of %d tokens (%d routed pairs, %.1f s) scaled by "
+                      "T/%d, plus its dispatch of all %d pairs (%.3f s); same seeded "
+                      "decode workload" % (n_tokens, T, n_tokens * K, t_fwd, n_tokens, T * K,
+                                           t_disp)}
+
+
+def copy_calibration(dev):
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 3}))
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE=%d)." % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synthetic as S
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+
+    cfg = S.CONFIGS[args.workload]
+    main_r = time_workload(cfg, args.steps, args.warmup, args.block_m, dev)
+    main_s = summarize(main_r)
+    print("# %s: %.4f ms/layer, %.1f GB/s (%.1f%% of HBM peak), gen %.1fs"
+          % (cfg["name"], main_s["ms_per_layer"], main_s["HBM_GB_s"], 100 * main_s["hbm_frac"],
+             main_r["gen_s"]), file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(main_r, args.cpu_tokens)
+        print("# cpu baseline: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
+    main_d = main_r.pop("d")
+    del main_d, main_r["tables"]
+    torch.cuda.empty_cache()
+
+    t4096 = None
+    if not args.no_t4096 and args.workload == 2:
+        r3 = time_workload(S.CONFIGS[3], args.steps, args.warmup, None, dev)
+        r3.pop("d")
+        r3.pop("tables")
+        torch.cuda.empty_cache()
+        t4096 = summarize(r3)
+        t4096["workload"] = S.CONFIGS[3]["name"]
+        print("# %s: %.4f ms/layer, %.2f TFLOP/s, %.1f GB/s"
+              % (S.CONFIGS[3]["name"], t4096["ms_per_layer"], t4096["TFLOP_s"],
+                 t4096["HBM_GB_s"]), file=sys.stderr, flush=True)
+
+    gu = main_s["kernels"]["gate_up"]
+    achieved = gu["GB_s"]
+    traffic = counter_traffic()
+    line = {
+        "metric": "routed-MoE fwd ms/layer + TFLOP/s & HBM GB/s vs peak at T=512, T=4096",
+        "value": main_s["ms_per_layer"],
+        "unit": "ms/layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": main_s["ms_per_layer"],
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == "bf16" else cfg["dtype"],
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init expert weights, "
+                "N(0,0.02) router, softmax top-k)",
+        "config": {"workload": cfg["name"], "T": cfg["T"], "d_hidden": cfg["H"],
+                   "d_expert": cfg["D"], "n_routed_experts": cfg["E"], "top_k": cfg["K"],
+                   "block_m": main_s["block_m"]},
+        "TFLOP_s": main_s["TFLOP_s"], "HBM_GB_s": main_s["HBM_GB_s"],
+        "hbm_frac": main_s["hbm_frac"], "mfma_frac": main_s["mfma_frac"],
+        "roofline_frac": main_s["roofline_frac"],
+        "roofline": {"bound": "hbm", "kernel": "grouped_gemm gate/up (SiLU*up fused)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algo_bytes_per_launch": gu["algo_bytes"],
+                     "avg_launch_ms": gu["ms"]},
+        "kernels": main_s["kernels"],
+        "t4096": t4096,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

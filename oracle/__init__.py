@@ -30,6 +30,8 @@ def lib():
         L = ctypes.CDLL(_build.LIB)
         vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = i32
         L.oracle_to_f32.argtypes = [i32, vp, f32p, i64]
         L.oracle_from_f32.argtypes = [i32, f32p, vp, i64]
         L.oracle_silu_mul.argtypes = [f32p, f32p, f32p, i64]
@@ -43,6 +45,11 @@ def lib():
         L.oracle_reduce.argtypes = [i32, vp, i64, i32p, f32p, i32, i32, i32, f32p]
         _lib = L
     return _lib
+
+
+def num_threads():
+    """oracle_num_threads: OpenMP threads the oracle's loops use."""
+    return int(lib().oracle_num_threads())
 
 
 def _ptr(a):

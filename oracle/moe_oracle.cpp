@@ -34,6 +34,8 @@
 #include <limits>
 #include <vector>
 
+#include <omp.h>
+
 namespace {
 
 // Storage codes of this file (an interface agreement with the tests only).
@@ -152,6 +154,9 @@ void expert_pair(int dt, const float* xrow, const void* wg, const void* wu,
 }  // namespace
 
 extern "C" {
+
+// Threads the OpenMP loops below use (reported with the CPU baseline).
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 // ------------------------------------------------------------ conversions --
 // Element-wise storage conversions, exported so the tests can pin them
