@@ -85,6 +85,11 @@ typedef enum moe_dtype { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2 } moe_dtype;
  *   topk_weights[p]         fp32 copy of the routing weights, token order [P]
  *   status[0]               0, or 1 if an id >= E was seen (it is then
  *                           treated as a masked slot)                    [1]
+ *   active_blocks[j]        the blocks that hold rows, in ascending order:
+ *                           expert e contributes blocks padded[e]/block_m
+ *                           + 0 .. ceil(group_sizes[e]/block_m) - 1
+ *                           (a scheduling list for the GEMMs) [num_blocks]
+ *   active_count[0]         the number of entries of active_blocks       [1]
  * Entries i >= n_valid of the sorted_* arrays are unspecified. A slot with a
  * negative id is masked: it is not counted and never read. The scan scratch
  * (chunk_counts, chunk_flags, pair_rank) is internal. moe_dispatch writes
@@ -102,6 +107,8 @@ typedef struct moe_tables {
   int32_t *token_topk_to_pos;
   float *topk_weights;
   int32_t *status;
+  int32_t *active_blocks;
+  int32_t *active_count;
   int32_t *chunk_counts; /* [num_chunks * E] */
   int32_t *chunk_flags;  /* [num_chunks]     */
   int32_t *pair_rank;    /* [P]              */

@@ -29,6 +29,7 @@ _TABLE_FIELDS = {
     "sorted_pair": ("P", torch.int32), "sorted_token": ("P", torch.int32),
     "sorted_weight": ("P", torch.float32), "token_topk_to_pos": ("P", torch.int32),
     "topk_weights": ("P", torch.float32), "status": ("one", torch.int32),
+    "active_blocks": ("num_blocks", torch.int32), "active_count": ("one", torch.int32),
 }
 
 

@@ -25,6 +25,7 @@ class MoeTablesStruct(ctypes.Structure):
         ("sorted_pair", ctypes.c_void_p), ("sorted_token", ctypes.c_void_p),
         ("sorted_weight", ctypes.c_void_p), ("token_topk_to_pos", ctypes.c_void_p),
         ("topk_weights", ctypes.c_void_p), ("status", ctypes.c_void_p),
+        ("active_blocks", ctypes.c_void_p), ("active_count", ctypes.c_void_p),
         ("chunk_counts", ctypes.c_void_p), ("chunk_flags", ctypes.c_void_p),
         ("pair_rank", ctypes.c_void_p),
     ]

@@ -59,8 +59,8 @@ moe_status check_table_sizes(int T, int K, int E, int block_m) {
 
 struct TableLayout {
   size_t group_sizes, group_offsets, group_padded_offsets, block_expert, sorted_pair,
-      sorted_token, sorted_weight, token_topk_to_pos, topk_weights, status, chunk_counts,
-      chunk_flags, pair_rank, total;
+      sorted_token, sorted_weight, token_topk_to_pos, topk_weights, status, active_blocks,
+      active_count, chunk_counts, chunk_flags, pair_rank, total;
   int num_blocks, num_chunks;
 };
 
@@ -85,6 +85,8 @@ TableLayout table_layout(int T, int K, int E, int block_m) {
   L.token_topk_to_pos = take(4 * P);
   L.topk_weights = take(4 * P);
   L.status = take(4);
+  L.active_blocks = take(4 * static_cast<size_t>(L.num_blocks));
+  L.active_count = take(4);
   L.chunk_counts = take(4 * static_cast<size_t>(L.num_chunks) * E);
   L.chunk_flags = take(4 * static_cast<size_t>(L.num_chunks));
   L.pair_rank = take(4 * P);
@@ -95,7 +97,8 @@ TableLayout table_layout(int T, int K, int E, int block_m) {
 bool tables_bound(const moe_tables* t) {
   return t && t->group_sizes && t->group_offsets && t->group_padded_offsets &&
          t->block_expert && t->sorted_pair && t->sorted_token && t->sorted_weight &&
-         t->token_topk_to_pos && t->topk_weights && t->status && t->chunk_counts &&
+         t->token_topk_to_pos && t->topk_weights && t->status && t->active_blocks &&
+         t->active_count && t->chunk_counts &&
          t->chunk_flags && t->pair_rank;
 }
 
@@ -173,6 +176,8 @@ moe_status moe_tables_bind(moe_tables* tables, void* buffer, size_t bytes, int T
   tables->token_topk_to_pos = reinterpret_cast<int32_t*>(b + L.token_topk_to_pos);
   tables->topk_weights = reinterpret_cast<float*>(b + L.topk_weights);
   tables->status = reinterpret_cast<int32_t*>(b + L.status);
+  tables->active_blocks = reinterpret_cast<int32_t*>(b + L.active_blocks);
+  tables->active_count = reinterpret_cast<int32_t*>(b + L.active_count);
   tables->chunk_counts = reinterpret_cast<int32_t*>(b + L.chunk_counts);
   tables->chunk_flags = reinterpret_cast<int32_t*>(b + L.chunk_flags);
   tables->pair_rank = reinterpret_cast<int32_t*>(b + L.pair_rank);

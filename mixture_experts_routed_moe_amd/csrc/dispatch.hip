@@ -17,7 +17,9 @@
 //   scan   one workgroup: an exclusive scan of every expert's column of
 //          chunk counts (the chunk prefix), then workgroup-wide scans over
 //          the experts for group_offsets and group_padded_offsets, then each
-//          expert writes its own range of block_expert.
+//          expert writes its own range of block_expert and its entries of the
+//          compact list of blocks that hold rows (active_blocks), which the
+//          GEMMs use to spread only real work over the chip.
 //   place  pos = group_offsets[e] + chunk_prefix[chunk][e] + rank, and the
 //          sorted_* arrays and token_topk_to_pos are written.
 // The order is stable in the flat slot index p = t*K + k by construction;
@@ -109,7 +111,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     int32_t* __restrict__ chunk_counts, const int32_t* __restrict__ chunk_flags, int C, int E,
     int BM, int num_blocks, int32_t* __restrict__ group_sizes,
     int32_t* __restrict__ group_offsets, int32_t* __restrict__ group_padded_offsets,
-    int32_t* __restrict__ block_expert, int32_t* __restrict__ status) {
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ status,
+    int32_t* __restrict__ active_blocks, int32_t* __restrict__ active_count) {
   __shared__ int s_wave[kWaves];
   const int e = threadIdx.x;   // E <= 1024: one expert per thread
   int bad = 0;
@@ -134,8 +137,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     }
   }
   const int padded_size = (e < E) ? ((cnt + 1 + BM - 1) / BM) * BM : 0;
+  const int n_active = (e < E) ? (cnt + BM - 1) / BM : 0;
   const int incl_off = block_inclusive_scan(e < E ? cnt : 0, s_wave);
   const int incl_pad = block_inclusive_scan(padded_size, s_wave);
+  const int incl_act = block_inclusive_scan(n_active, s_wave);
   if (e < E) {
     const int pad_start = incl_pad - padded_size;
     group_sizes[e] = cnt;
@@ -144,6 +149,9 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const int b0 = pad_start / BM;
     const int b1 = (e + 1 < E) ? incl_pad / BM : num_blocks;
     for (int b = b0; b < b1; ++b) block_expert[b] = e;
+    const int a0 = incl_act - n_active;
+    for (int j = 0; j < n_active; ++j) active_blocks[a0 + j] = b0 + j;
+    if (e == E - 1) active_count[0] = incl_act;
   }
 }
 
@@ -181,7 +189,8 @@ hipError_t launch_dispatch(const int32_t* topk_ids, const float* topk_weights,
                      topk_ids, P, t.E, nbits, t.chunk_counts, t.pair_rank, t.chunk_flags);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, stream, t.chunk_counts,
                      t.chunk_flags, t.num_chunks, t.E, t.block_m, t.num_blocks, t.group_sizes,
-                     t.group_offsets, t.group_padded_offsets, t.block_expert, t.status);
+                     t.group_offsets, t.group_padded_offsets, t.block_expert, t.status,
+                     t.active_blocks, t.active_count);
   hipLaunchKernelGGL(dispatch_place_kernel, dim3(t.num_chunks), dim3(kChunk), 0, stream,
                      topk_ids, topk_weights, P, t.K, t.E, t.chunk_counts, t.group_offsets,
                      t.pair_rank, t.sorted_pair, t.sorted_token, t.sorted_weight,

@@ -34,9 +34,10 @@
 //     the MFMAs of chunk c.
 //   * Row groups of 32 rows with no valid row skip their MFMAs, so a block
 //     with 16 rows of a 32/64/128-row tile costs one row group of MFMA work.
-//   * Blocks are mapped XCD-aware: workgroup L runs on XCD L % 8, so the
-//     natural tile order (row block major, column tile minor) is dealt out in
-//     contiguous ranges per XCD. The column tiles of one row block then share
+//   * Only blocks that hold rows are scheduled (the dispatch's active-block
+//     list), and they are mapped XCD-aware: workgroup L runs on XCD L % 8, so
+//     the natural tile order (active block major, column tile minor) is dealt
+//     out in equal contiguous ranges per XCD. The column tiles of one row block then share
 //     the A rows in that XCD's L2, and the blocks of one expert that spill
 //     into a second row block run at the same time on the same XCD, so their
 //     second read of the expert's weights is served by L2.
@@ -61,7 +62,9 @@ struct GemmArgs {
   const int32_t* group_offsets;
   const int32_t* group_padded_offsets;
   const int32_t* block_expert;
-  int n, kd, block_m, num_blocks, n_tiles;
+  const int32_t* active_blocks;
+  const int32_t* active_count;
+  int n, kd, block_m, n_tiles;
 };
 
 template <int DT>
@@ -89,12 +92,15 @@ template <int DT, int RG, bool GATEUP>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][32 * RG][kLdsRow];
 
-  const int total = g.num_blocks * g.n_tiles;
-  const int per_xcd = gridDim.x >> 3;
+  // Only blocks that hold rows are scheduled: the grid is sized for every
+  // block, and workgroups past the active work exit at once.
+  const int total = g.active_count[0] * g.n_tiles;
+  const int per_xcd = (total + 7) >> 3;
   const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (natural >= total) return;
-  const int bx = natural / g.n_tiles;
-  const int nt = natural - bx * g.n_tiles;
+  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
+  const int ab = natural / g.n_tiles;
+  const int nt = natural - ab * g.n_tiles;
+  const int bx = g.active_blocks[ab];
 
   const int e = g.block_expert[bx];
   const int row_in_group = bx * g.block_m - g.group_padded_offsets[e];
@@ -248,12 +254,13 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
   g.group_offsets = t.group_offsets;
   g.group_padded_offsets = t.group_padded_offsets;
   g.block_expert = t.block_expert;
+  g.active_blocks = t.active_blocks;
+  g.active_count = t.active_count;
   g.n = p.n;
   g.kd = p.kd;
   g.block_m = t.block_m;
-  g.num_blocks = t.num_blocks;
   g.n_tiles = p.n / (GATEUP ? 128 : 256);
-  const int64_t total = static_cast<int64_t>(g.num_blocks) * g.n_tiles;
+  const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
   const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
   if (t.block_m <= 32) {
     hipLaunchKernelGGL((grouped_gemm_kernel<DT, 1, GATEUP>), dim3(grid), dim3(kThreads), 0,

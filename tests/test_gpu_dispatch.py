@@ -36,6 +36,12 @@ def _compare(ids, w, E, BM):
     assert np.array_equal(got_w, ref["sorted_weight"][:n].view(np.uint32))
     wt = np.ones(ids.size, np.float32) if w is None else w.reshape(-1)
     assert np.array_equal(t.topk_weights.cpu().numpy().view(np.uint32), wt.view(np.uint32))
+    # the scheduling list: every block that holds rows, ascending
+    sizes, pad = ref["group_sizes"], ref["group_padded_offsets"]
+    active = [pad[e] // BM + j for e in range(E) for j in range(-(-int(sizes[e]) // BM))]
+    cnt = int(t.active_count.item())
+    assert cnt == len(active)
+    assert t.active_blocks[:cnt].cpu().tolist() == active
     return t
 
 
