@@ -60,10 +60,11 @@ def _check_tensor(t, name, dtype=None, ndim=None, device=None):
 
 def default_block_m(T, K, E):
     """Row-block size of the tables: the power of two >= twice the mean rows
-    per expert, clamped to [16, 128], so a typical expert fits in one block."""
+    per expert, clamped to [16, 256], so a typical expert fits in one block
+    and its weights are streamed once."""
     avg = max(1.0, T * K / E)
     bm = 1 << max(0, math.ceil(math.log2(2 * avg)))
-    return int(min(128, max(16, bm)))
+    return int(min(256, max(16, bm)))
 
 
 class MoeTables:

@@ -117,7 +117,8 @@ def test_workspace_layout():
 def test_default_block_m():
     assert mr.default_block_m(512, 8, 256) == 32      # ~16 rows per expert
     assert mr.default_block_m(512, 8, 128) == 64
-    assert mr.default_block_m(4096, 8, 256) == 128
+    assert mr.default_block_m(4096, 8, 256) == 256
+    assert mr.default_block_m(2048, 8, 256) == 128
     assert mr.default_block_m(1, 1, 256) == 16
 
 
