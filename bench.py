@@ -45,7 +45,7 @@ def parse_args():
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--no-t4096", action="store_true", help="skip the T=4096 prefill case")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=128,
+    ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens of the decode workload the oracle runs for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")

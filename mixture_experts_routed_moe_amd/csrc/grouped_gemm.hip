@@ -42,6 +42,9 @@
 //     into a second row block run at the same time on the same XCD, so their
 //     second read of the expert's weights is served by L2.
 
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -54,10 +57,17 @@ constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
 #ifndef MOE_STAGES_RG1
 #define MOE_STAGES_RG1 4
 #endif
+#ifndef MOE_STAGES_RG1_DOWN
+#define MOE_STAGES_RG1_DOWN 2
+#endif
 #ifndef MOE_STAGES_RG2
 #define MOE_STAGES_RG2 4
 #endif
-constexpr int kStagesRG1 = MOE_STAGES_RG1;   // pipeline depth, blocks of <= 32 rows
+// Pipeline depths (chunks in flight), measured on MI355X: blocks of <= 32
+// rows stream gate/up best at depth 4 and down (half the bytes per column
+// tile, more workgroups) at depth 2.
+constexpr int kStagesRG1 = MOE_STAGES_RG1;
+constexpr int kStagesRG1Down = MOE_STAGES_RG1_DOWN;
 constexpr int kStagesRG2 = MOE_STAGES_RG2;   // 64-row blocks
 #ifndef MOE_STAGES_ROWSPLIT
 #define MOE_STAGES_ROWSPLIT 4
@@ -105,6 +115,20 @@ __device__ __forceinline__ u32x4 load16_stream(const uint16_t* p) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+template <int N>
+using int_c = std::integral_constant<int, N>;
+
+// Calls f(int_c<0>{}), ..., f(int_c<N-1>{}): a loop whose index is a
+// compile-time constant in every iteration (register-ring slots stay static).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(int_c<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // One pass over the reduction for NA active row groups (NA*32 rows) of the
 // block, with a software pipeline of depth S: the A share and the B
 // fragments of chunk c+S-1 are loaded while chunk c is multiplied. The loads
@@ -112,10 +136,8 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // order, waiting for the A share of chunk c+1 (to stage it in LDS) never
 // waits for B fragments of later chunks, so S-1 chunks of weights stay in
 // flight across the per-chunk barrier. The loop body is straight-line (no
-// branch touches the accumulators, so they stay in place): prefetches past
-// the last chunk re-read the last chunk (already in L2), and A rows past the
-// block's rows read a valid row whose products are never stored. S divides
-// the chunk count.
+// branch touches the accumulators, so they stay in place); the last S
+// chunks are a peeled copy without prefetches. S divides the chunk count.
 template <int DT, int NA, int RG, bool GATEUP, int S>
 __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[32 * RG][kLdsRow],
                                           const uint16_t* const* asrc,
@@ -132,7 +154,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
   u32x4 bring[S][2][4];
 
   auto load_chunk = [&](int c, int slot) {
-    int cc = min(c, nchunks - 1) + rot;
+    int cc = c + rot;
     if (cc >= nchunks) cc -= nchunks;
     const int64_t off = static_cast<int64_t>(cc) * kChunkK;
 #pragma unroll
@@ -157,26 +179,34 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
   stage_a(0, 0);
   __syncthreads();
 
-  for (int c0 = 0; c0 < nchunks; c0 += S) {
+  // One chunk: prefetch chunk c+S-1 (only while it exists: the last group of
+  // S chunks is peeled, so nothing past the end is ever loaded), multiply
+  // chunk c, stage chunk c+1's A share, barrier.
+  auto step = [&](int c, auto U, auto PREFETCH, auto STAGE) {
+    constexpr int u = decltype(U)::value;
+    if constexpr (decltype(PREFETCH)::value) load_chunk(c + S - 1, (u + S - 1) % S);
+    constexpr int buf = u & 1;   // S is even, so c & 1 == u & 1
 #pragma unroll
-    for (int u = 0; u < S; ++u) {
-      const int c = c0 + u;
-      load_chunk(c + S - 1, (u + S - 1) % S);
-      const int buf = u & 1;   // S is even or 1, so c & 1 == u & 1
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int q = 0; q < NA; ++q) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(&lds_a[buf][q * 32 + lr][lh * 32 + t * 8]);
-          acc[q][0] = mfma32x32x16<DT>(a, bring[u][0][t], acc[q][0]);
-          acc[q][1] = mfma32x32x16<DT>(a, bring[u][1][t], acc[q][1]);
-        }
+      for (int q = 0; q < NA; ++q) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(&lds_a[buf][q * 32 + lr][lh * 32 + t * 8]);
+        acc[q][0] = mfma32x32x16<DT>(a, bring[u][0][t], acc[q][0]);
+        acc[q][1] = mfma32x32x16<DT>(a, bring[u][1][t], acc[q][1]);
       }
-      stage_a((u + 1) % S, buf ^ 1);
-      __syncthreads();
     }
+    if constexpr (decltype(STAGE)::value) stage_a((u + 1) % S, buf ^ 1);
+    __syncthreads();
+  };
+  int c0 = 0;
+  for (; c0 + S < nchunks; c0 += S) {
+    static_for<S>([&](auto U) { step(c0 + U, U, std::true_type{}, std::true_type{}); });
   }
+  static_for<S>([&](auto U) {
+    step(c0 + U, U, std::bool_constant<decltype(U)::value == 0>{},
+         std::bool_constant<(decltype(U)::value < S - 1)>{});
+  });
 
   // Epilogue. MFMA 32x32 accumulator layout: lane l holds column l % 32 and,
   // in register i, row 8*(i/4) + 4*(l/32) + i%4 of the 32x32 tile.
@@ -313,7 +343,7 @@ __device__ __forceinline__ void rowsplit_pass(const GemmArgs& g,
   u32x4 bring[S][kBVec];
 
   auto load_chunk = [&](int c, int slot) {
-    const int64_t off = static_cast<int64_t>(min(c, nchunks - 1)) * kChunkK;
+    const int64_t off = static_cast<int64_t>(c) * kChunkK;
     if constexpr (HAS_ROWS) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) aring[slot][t] = load16(a_ptr + off + t * 8);
@@ -333,27 +363,32 @@ __device__ __forceinline__ void rowsplit_pass(const GemmArgs& g,
   stage_b(0, 0);
   __syncthreads();
 
-  for (int c0 = 0; c0 < nchunks; c0 += S) {
+  auto step = [&](int c, auto U, auto PREFETCH, auto STAGE) {
+    constexpr int u = decltype(U)::value;
+    if constexpr (decltype(PREFETCH)::value) load_chunk(c + S - 1, (u + S - 1) % S);
+    constexpr int buf = u & 1;
+    if constexpr (HAS_ROWS) {
 #pragma unroll
-    for (int u = 0; u < S; ++u) {
-      const int c = c0 + u;
-      load_chunk(c + S - 1, (u + S - 1) % S);
-      const int buf = u & 1;
-      if constexpr (HAS_ROWS) {
+      for (int t = 0; t < 4; ++t) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4 b =
-                *reinterpret_cast<const u32x4*>(&lds_b[buf][j * 32 + lr][lh * 32 + t * 8]);
-            acc[j] = mfma32x32x16<DT>(aring[u][t], b, acc[j]);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 b =
+              *reinterpret_cast<const u32x4*>(&lds_b[buf][j * 32 + lr][lh * 32 + t * 8]);
+          acc[j] = mfma32x32x16<DT>(aring[u][t], b, acc[j]);
         }
       }
-      stage_b((u + 1) % S, buf ^ 1);
-      __syncthreads();
     }
+    if constexpr (decltype(STAGE)::value) stage_b((u + 1) % S, buf ^ 1);
+    __syncthreads();
+  };
+  int c0 = 0;
+  for (; c0 + S < nchunks; c0 += S) {
+    static_for<S>([&](auto U) { step(c0 + U, U, std::true_type{}, std::true_type{}); });
   }
+  static_for<S>([&](auto U) {
+    step(c0 + U, U, std::bool_constant<decltype(U)::value == 0>{},
+         std::bool_constant<(decltype(U)::value < S - 1)>{});
+  });
 
   if constexpr (HAS_ROWS) {
 #pragma unroll
@@ -487,7 +522,7 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
     return hipGetLastError();
   }
   if (t.block_m <= 32) {
-    launch_rg<DT, 1, GATEUP, kStagesRG1>(grid, g, stream);
+    launch_rg<DT, 1, GATEUP, GATEUP ? kStagesRG1 : kStagesRG1Down>(grid, g, stream);
   } else {
     launch_rg<DT, 2, GATEUP, kStagesRG2>(grid, g, stream);
   }
