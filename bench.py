@@ -49,6 +49,8 @@ def parse_args():
                     help="tokens of the decode workload the oracle runs for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--dump-routing", default=None, metavar="FILE",
+                    help="only write the workload's routing (ids, weights) for moe_bench_driver")
     return ap.parse_args()
 
 
@@ -208,6 +210,25 @@ def cpu_baseline(r, n_tokens):
                                            t_disp)}
 
 
+def dump_routing(cfg, block_m, path):
+    """Write {magic, T, K, E, H, D, dtype, block_m} + ids + weights for the C++
+    driver (mixture_experts_routed_moe_amd/moe_bench_driver routing FILE)."""
+    import numpy as np
+
+    import mixture_experts_routed_moe_amd as mr
+    import synthetic as S
+    d = S.make_moe_inputs(cfg, device="cpu", weights=False)
+    T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
+    block_m = block_m or mr.default_block_m(T, K, E)
+    code = {"f16": 0, "bf16": 1, "f32": 2}[cfg["dtype"]]
+    hdr = np.array([0x4d6f4531, T, K, E, H, D, code, block_m], np.int32)
+    with open(path, "wb") as f:
+        f.write(hdr.tobytes())
+        f.write(d["topk_ids"].numpy().astype(np.int32).tobytes())
+        f.write(d["topk_weights"].numpy().astype(np.float32).tobytes())
+    print(json.dumps({"routing_dump": path, "workload": cfg["name"], "block_m": int(block_m)}))
+
+
 def copy_calibration(dev):
     import torch
     n = 1 << 30
@@ -227,8 +248,11 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d, WORLD_SIZE=%d)." % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
-    import torch
     import synthetic as S
+    if args.dump_routing:
+        dump_routing(S.CONFIGS[args.workload], args.block_m, args.dump_routing)
+        return
+    import torch
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(dev)

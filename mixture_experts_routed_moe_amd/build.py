@@ -14,6 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_routed.so")
+DRIVER = os.path.join(HERE, "moe_bench_driver")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -55,6 +56,17 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    # The C++ driver of the C ABI (profiler passes without Python in the process).
+    dtmp = DRIVER + ".tmp"
+    cmd = [HIPCC, "-x", "hip", "--offload-arch=" + ARCH] + DEVICE_FLAGS + COMMON + [
+        os.path.join(CSRC, "bench_driver.hip"), "-o", dtmp, "-L" + HERE, "-lmoe_routed",
+        "-Wl,-rpath,$ORIGIN"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("driver build failed:\n%s%s" % (res.stdout, res.stderr))
+    os.replace(dtmp, DRIVER)
     return LIB
 
 
