@@ -152,7 +152,9 @@ moe_status moe_dispatch(const int32_t* topk_ids, const float* topk_weights,
  *           u = x[sorted_token[i]] . w_up[e, j], e the expert of row i,
  *           SiLU(g) = g / (1 + exp(-g)), fp32 accumulation, R = rounding to
  *           dtype. Rows >= n_valid are not written.
- *   dtype   MOE_BF16 or MOE_F16.
+ *   dtype   MOE_BF16 or MOE_F16 (MFMA kernels), or MOE_F32 (the debug path:
+ *           fp32 inputs and intermediates, no rounding, vector-ALU kernel
+ *           with each dot product one fmaf chain in ascending order).
  * Requires H % 256 == 0 and D % 128 == 0.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP. */
 moe_status moe_expert_gate_up(const void* x, const void* w_gate, const void* w_up,

@@ -125,8 +125,8 @@ def moe_dispatch(topk_ids, topk_weights, num_experts, block_m=None, tables=None)
 
 def _expert_shapes(x_or_h, w_a, w_b, w_down, tables, gate_up):
     dt = x_or_h.dtype
-    _require(dt in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
-             "expert GEMMs take float16 or bfloat16 (got %s)" % dt)
+    _require(dt in (torch.float16, torch.bfloat16, torch.float32), MOE_ERR_DTYPE,
+             "expert GEMMs take float16, bfloat16 or float32 (got %s)" % dt)
     E = tables.E
     if gate_up:
         T, H = x_or_h.shape

@@ -39,6 +39,8 @@ bool block_m_ok(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 |
 
 bool is_16bit(int dt) { return dt == MOE_F16 || dt == MOE_BF16; }
 
+bool is_float(int dt) { return is_16bit(dt) || dt == MOE_F32; }
+
 size_t dtype_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
 moe_status check_table_sizes(int T, int K, int E, int block_m) {
@@ -111,8 +113,9 @@ moe_status hip_status(hipError_t err, const char* what) {
 
 moe_status check_expert_shapes(const moe_tables* t, int H, int D, int dtype) {
   if (!tables_bound(t)) return fail(MOE_ERR_NULL, "tables are NULL or not bound");
-  if (!is_16bit(dtype)) {
-    return fail(MOE_ERR_DTYPE, "expert GEMMs take MOE_F16 or MOE_BF16 (got dtype %d)", dtype);
+  if (!is_float(dtype)) {
+    return fail(MOE_ERR_DTYPE, "expert GEMMs take MOE_F16, MOE_BF16 or MOE_F32 (got dtype %d)",
+                dtype);
   }
   if (H <= 0 || H % 256 != 0) return fail(MOE_ERR_SHAPE, "H must be a positive multiple of 256 (got %d)", H);
   if (D <= 0 || D % 128 != 0) return fail(MOE_ERR_SHAPE, "D must be a positive multiple of 128 (got %d)", D);
@@ -217,7 +220,7 @@ moe_status moe_expert_down(const void* h, const void* w_down, const moe_tables* 
 }
 
 size_t moe_forward_workspace_expert_out_offset(int T, int K, int H, int D, int dtype) {
-  if (T < 1 || K < 1 || H <= 0 || D <= 0 || !is_16bit(dtype)) return 0;
+  if (T < 1 || K < 1 || H <= 0 || D <= 0 || !is_float(dtype)) return 0;
   return align_up(ws_h_bytes(T, K, D, dtype));
 }
 

@@ -532,11 +532,13 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
 }  // namespace
 
 hipError_t launch_gate_up(const GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  if (p.dtype == kF32) return launch_gate_up_f32(p, t, stream);
   if (p.dtype == kBF16) return launch_typed<kBF16, true>(p, t, stream);
   return launch_typed<kF16, true>(p, t, stream);
 }
 
 hipError_t launch_down(const GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  if (p.dtype == kF32) return launch_down_f32(p, t, stream);
   if (p.dtype == kBF16) return launch_typed<kBF16, false>(p, t, stream);
   return launch_typed<kF16, false>(p, t, stream);
 }

@@ -20,11 +20,13 @@ struct GemmProblem {
   void* c;               // gate/up: h [P, N]; down: expert_out [P, N]
   int n;                 // output columns (D for gate/up, H for down)
   int kd;                // reduction length (H for gate/up, D for down)
-  int dtype;             // kF16 / kBF16
+  int dtype;             // kF16 / kBF16 / kF32
 };
 
 hipError_t launch_gate_up(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_gate_up_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_down_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 
 hipError_t launch_reduce(const void* x, int64_t rows, const int32_t* pos, const float* w, int T,
                          int K, int H, int in_dtype, int out_dtype, void* y, hipStream_t stream);

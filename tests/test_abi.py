@@ -96,7 +96,7 @@ def test_calls_reject_bad_arguments_before_launching():
                                 1 << 30, fake, None) == 2
     assert L.moe_routed_forward(fake, fake, fake, fake, ctypes.byref(s), 256, 100, 1, fake,
                                 1 << 30, fake, None) == 2
-    assert L.moe_routed_forward(fake, fake, fake, fake, ctypes.byref(s), 256, 128, 2, fake,
+    assert L.moe_routed_forward(fake, fake, fake, fake, ctypes.byref(s), 256, 128, 7, fake,
                                 1 << 30, fake, None) == 3
     need = L.moe_forward_workspace_bytes(8, 2, 256, 128, 1)
     assert need > 0

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import ORACLE_DT, assert_close_16, gpu_available, metrics, storage
+from helpers import ORACLE_DT, REL_L2_32, assert_close_16, gpu_available, metrics, storage
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -157,13 +157,42 @@ def test_forward_argument_errors():
     with pytest.raises(mr.MoeError) as ei:       # w_up of another shape
         mr.moe_routed_forward(d["x"], d["w_gate"], d["w_up"][:, :64].contiguous(), d["w_down"], tables)
     assert ei.value.status == 2
-    with pytest.raises(mr.MoeError) as ei:       # fp32 inputs
-        mr.moe_routed_forward(d["x"].float(), d["w_gate"].float(), d["w_up"].float(),
-                              d["w_down"].float(), tables)
+    with pytest.raises(mr.MoeError) as ei:       # float64 inputs
+        mr.moe_routed_forward(d["x"].double(), d["w_gate"].double(), d["w_up"].double(),
+                              d["w_down"].double(), tables)
+    assert ei.value.status == 3
+    with pytest.raises(mr.MoeError) as ei:       # mixed dtypes
+        mr.moe_routed_forward(d["x"], d["w_gate"].float(), d["w_up"], d["w_down"], tables)
     assert ei.value.status == 3
     with pytest.raises(mr.MoeError) as ei:       # weights of the wrong dtype
         mr.moe_dispatch(d["topk_ids"], d["topk_weights"].half(), 4)
     assert ei.value.status == 3
+
+
+# ------------------------------------------------------------- fp32 path ---
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_forward_fp32_debug_path(ci):
+    # The fp32 build of the forward against the oracle's fp32 storage (no
+    # intermediate rounding): rel-L2 <= 1e-4.
+    cfg = dict(S.CONFIGS[ci], dtype="f32")
+    d = S.make_moe_inputs(cfg, device=DEV)
+    tables, h, eo, y = _run(d)
+    y_ref, hp, ep = _oracle(d)
+    got = y.cpu().numpy()
+    assert not np.isnan(got).any()
+    mabs, rel = metrics(got, y_ref)
+    assert rel <= REL_L2_32, (mabs, rel)
+    _check_pairs(tables, h, eo, hp, ep, cfg["K"])
+
+
+@pytest.mark.parametrize("block_m", [16, 64, 256])
+def test_forward_fp32_ragged(block_m):
+    d = _custom(T=97, H=512, D=384, E=6, K=3, dtype="f32", seed=21, mask=0.15, hot=2)
+    tables, h, eo, y = _run(d, block_m=block_m)
+    y_ref, hp, ep = _oracle(d)
+    mabs, rel = metrics(y.cpu().numpy(), y_ref)
+    assert rel <= REL_L2_32, (mabs, rel)
 
 
 # ------------------------------------------------------------ full sizes ---
