@@ -8,7 +8,7 @@ Thin numpy/ctypes wrappers over ``moe_oracle.cpp``; every wrapper names the
 C function it calls. Arrays are host numpy arrays. 16-bit inputs are passed
 as ``uint16`` bit patterns (or numpy ``float16`` for fp16); fp32 as float32.
 
-Dtype codes: 0 = fp16, 1 = bf16, 2 = fp32.
+Dtype codes: 0 = fp16, 1 = bf16, 2 = fp32, 3 = FP8 E4M3 (OCP "fn"; reduce only).
 """
 import ctypes
 import os
@@ -17,7 +17,7 @@ import numpy as np
 
 from . import build as _build
 
-F16, BF16, F32 = 0, 1, 2
+F16, BF16, F32, FP8 = 0, 1, 2, 3
 
 _lib = None
 
@@ -43,6 +43,8 @@ def lib():
         L.oracle_moe_forward.argtypes = [i32, vp, vp, vp, vp, i32p, f32p, i32, i32, i32,
                                          i32, i32, i32p, i32, f32p, f32p, f32p]
         L.oracle_reduce.argtypes = [i32, vp, i64, i32p, f32p, i32, i32, i32, f32p]
+        L.oracle_reduce_scaled.argtypes = [i32, vp, i64, i32p, f32p, f32p, f32p, i32, i32, i32,
+                                           f32p]
         _lib = L
     return _lib
 
@@ -61,9 +63,11 @@ def _c(a, dtype):
 
 
 def _storage(a, dt):
-    """Contiguous storage array for dtype code dt (uint16 bits or float32)."""
+    """Contiguous storage array for dtype code dt (uint8 / uint16 bits or float32)."""
     if dt == F32:
         return _c(a, np.float32)
+    if dt == FP8:
+        return _c(a, np.uint8)
     if a.dtype == np.float16:
         return _c(a, np.float16).view(np.uint16)
     return _c(a, np.uint16)
@@ -80,7 +84,7 @@ def to_f32(bits, dt):
 def from_f32(x, dt):
     """oracle_from_f32: fp32 -> storage (round to nearest even); uint16 bits for 16-bit."""
     x = _c(x, np.float32)
-    out = np.empty(x.shape, np.float32 if dt == F32 else np.uint16)
+    out = np.empty(x.shape, {F32: np.float32, FP8: np.uint8}.get(dt, np.uint16))
     assert lib().oracle_from_f32(dt, _ptr(x), _ptr(out), x.size) == 0
     return out
 
@@ -160,15 +164,22 @@ def moe_forward(dt, x, wg, wu, wd, ids, w, tokens=None, want_pairs=False):
     return (y, hp, ep) if want_pairs else y
 
 
-def reduce(dt, X, pos, w=None):
-    """oracle_reduce: y [T, H] fp32 = sum_k w[t,k] * X[pos[t,k]] over pos >= 0."""
+def reduce(dt, X, pos, w=None, x_sf=None, sf=None):
+    """oracle_reduce / oracle_reduce_scaled: y [T, H] fp32 =
+    sf[t] * sum_k (w[t,k] * x_sf[pos[t,k]]) * X[pos[t,k]] over pos >= 0."""
     X = _storage(X, dt)
     pos = _c(pos, np.int32)
     T, K = pos.shape
     R, H = X.shape
     w = None if w is None else _c(w, np.float32)
     y = np.empty((T, H), np.float32)
-    rc = lib().oracle_reduce(dt, _ptr(X), R, _ptr(pos), _ptr(w), T, K, H, _ptr(y))
+    if x_sf is None and sf is None:
+        rc = lib().oracle_reduce(dt, _ptr(X), R, _ptr(pos), _ptr(w), T, K, H, _ptr(y))
+    else:
+        xs = None if x_sf is None else _c(x_sf, np.float32)
+        s = None if sf is None else _c(sf, np.float32)
+        rc = lib().oracle_reduce_scaled(dt, _ptr(X), R, _ptr(pos), _ptr(w), _ptr(xs), _ptr(s),
+                                        T, K, H, _ptr(y))
     if rc != 0:
         raise ValueError("oracle_reduce rejected its arguments")
     return y

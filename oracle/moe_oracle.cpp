@@ -42,6 +42,7 @@ namespace {
 constexpr int kF16 = 0;
 constexpr int kBF16 = 1;
 constexpr int kF32 = 2;
+constexpr int kFP8 = 3;   // OCP FP8 E4M3 "fn"
 
 // ---------------------------------------------------------------- dtypes ---
 
@@ -106,8 +107,46 @@ uint16_t float_to_f16_bits(float f) {
   return static_cast<uint16_t>(sign | (biased << 10) | (static_cast<int>(q) - 1024));
 }
 
+// OCP FP8 E4M3 ("fn") -> binary32 (exact), from the format definition:
+// 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; exponent 0 holds
+// subnormals; S.1111.111 is NaN; there are no infinities.
+float fp8e4m3_bits_to_float(uint8_t b) {
+  const int sign = (b >> 7) & 1;
+  const int expo = (b >> 3) & 0xf;
+  const int frac = b & 7;
+  float v;
+  if (expo == 15 && frac == 7) {
+    v = std::numeric_limits<float>::quiet_NaN();
+  } else if (expo == 0) {
+    v = std::ldexp(static_cast<float>(frac), -9);
+  } else {
+    v = std::ldexp(static_cast<float>(frac | 8), expo - 10);
+  }
+  return sign ? -v : v;
+}
+
+// binary32 -> FP8 E4M3 "fn", round to nearest even; magnitudes at or above
+// the largest finite value (448), infinities included, saturate to +-448.
+uint8_t float_to_fp8e4m3_bits(float f) {
+  const uint8_t sign = std::signbit(f) ? 0x80 : 0x00;
+  if (std::isnan(f)) return static_cast<uint8_t>(sign | 0x7f);
+  const double a = std::fabs(static_cast<double>(f));
+  if (a >= 448.0) return static_cast<uint8_t>(sign | 0x7e);
+  if (a < std::ldexp(1.0, -6)) {
+    const double q = std::nearbyint(a * std::ldexp(1.0, 9));   // [0, 8]
+    return static_cast<uint8_t>(sign | static_cast<int>(q));
+  }
+  int e2;
+  std::frexp(a, &e2);
+  int unb = e2 - 1;                                              // [-6, 8]
+  double q = std::nearbyint(a * std::ldexp(1.0, 3 - unb));      // [8, 16]
+  if (q >= 16.0) { q = 8.0; unb += 1; }
+  return static_cast<uint8_t>(sign | ((unb + 7) << 3) | (static_cast<int>(q) - 8));
+}
+
 float load_elem(int dt, const void* base, int64_t i) {
   if (dt == kF32) return static_cast<const float*>(base)[i];
+  if (dt == kFP8) return fp8e4m3_bits_to_float(static_cast<const uint8_t*>(base)[i]);
   const uint16_t b = static_cast<const uint16_t*>(base)[i];
   return dt == kBF16 ? bf16_bits_to_float(b) : f16_bits_to_float(b);
 }
@@ -121,6 +160,7 @@ float round_to(int dt, float v) {
 }
 
 bool dtype_ok(int dt) { return dt == kF16 || dt == kBF16 || dt == kF32; }
+bool reduce_dtype_ok(int dt) { return dtype_ok(dt) || dt == kFP8; }
 
 // SiLU(g) = g * sigmoid(g) = g / (1 + e^-g). [A] stage-1 writes sigmoid with
 // exp2(-g*log2 e); the value is the same function, written here with expf.
@@ -162,15 +202,16 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 // Element-wise storage conversions, exported so the tests can pin them
 // against library conversions and hand-made tie cases.
 int oracle_to_f32(int dt, const void* in, float* out, int64_t n) {
-  if (!dtype_ok(dt)) return -1;
+  if (!reduce_dtype_ok(dt)) return -1;
   for (int64_t i = 0; i < n; ++i) out[i] = load_elem(dt, in, i);
   return 0;
 }
 
 int oracle_from_f32(int dt, const float* in, void* out, int64_t n) {
-  if (!dtype_ok(dt)) return -1;
+  if (!reduce_dtype_ok(dt)) return -1;
   for (int64_t i = 0; i < n; ++i) {
     if (dt == kF32) static_cast<float*>(out)[i] = in[i];
+    else if (dt == kFP8) static_cast<uint8_t*>(out)[i] = float_to_fp8e4m3_bits(in[i]);
     else if (dt == kBF16) static_cast<uint16_t*>(out)[i] = float_to_bf16_bits(in[i]);
     else static_cast<uint16_t*>(out)[i] = float_to_f16_bits(in[i]);
   }
@@ -332,14 +373,19 @@ int oracle_moe_forward(int dt, const void* x, const void* wg, const void* wu,
 }
 
 // -------------------------------------------------------- weighted reduce --
-// moe_reduce_fused ([C] sections 1-2):
-//   y[t, :] = sum over k ascending with pos[t,k] >= 0 of w[t,k] * X[pos[t,k], :]
-// fp32 accumulation with fused multiply-add; w == NULL means all-ones
-// weights. X is [R, H] in dtype dt; y is [T, H] fp32. Rows named by masked
+// moe_reduce_fused ([C] sections 1-2) and its scaled variants ([C] section 1
+// and the commit note on the scaled variants: with_x_sf multiplies once per
+// routed slot, with_sf once per output element):
+//   y[t, :] = sf[t] * sum over k ascending with pos[t,k] >= 0 of
+//             (w[t,k] * x_sf[pos[t,k]]) * X[pos[t,k], :]
+// fp32 accumulation with fused multiply-add; w, x_sf, sf == NULL mean ones.
+// x_sf is indexed by the expanded row (the row of X), sf by token. X is
+// [R, H] in dtype dt (16-bit, fp32 or FP8 E4M3); y is [T, H] fp32 (cast it
+// with oracle_from_f32 for a 16-bit or FP8 output). Rows named by masked
 // slots are never read. Returns -1 when a position is >= R.
-int oracle_reduce(int dt, const void* X, int64_t R, const int32_t* pos,
-                  const float* w, int T, int K, int H, float* y) {
-  if (!dtype_ok(dt) || T < 0 || K <= 0 || H <= 0 || R < 0) return -1;
+int oracle_reduce_scaled(int dt, const void* X, int64_t R, const int32_t* pos, const float* w,
+                         const float* x_sf, const float* sf, int T, int K, int H, float* y) {
+  if (!reduce_dtype_ok(dt) || T < 0 || K <= 0 || H <= 0 || R < 0) return -1;
   const int64_t P = static_cast<int64_t>(T) * K;
   for (int64_t s = 0; s < P; ++s) {
     if (pos[s] >= R) return -1;
@@ -352,13 +398,22 @@ int oracle_reduce(int dt, const void* X, int64_t R, const int32_t* pos,
       const int64_t slot = static_cast<int64_t>(t) * K + k;
       const int32_t p = pos[slot];
       if (p < 0) continue;
-      const float wk = w ? w[slot] : 1.0f;
+      float wk = w ? w[slot] : 1.0f;
+      if (x_sf) wk = wk * x_sf[p];
       for (int c = 0; c < H; ++c) {
         yt[c] = std::fma(wk, load_elem(dt, X, static_cast<int64_t>(p) * H + c), yt[c]);
       }
     }
+    if (sf) {
+      for (int c = 0; c < H; ++c) yt[c] = yt[c] * sf[t];
+    }
   }
   return 0;
+}
+
+int oracle_reduce(int dt, const void* X, int64_t R, const int32_t* pos, const float* w, int T,
+                  int K, int H, float* y) {
+  return oracle_reduce_scaled(dt, X, R, pos, w, nullptr, nullptr, T, K, H, y);
 }
 
 }  // extern "C"
