@@ -44,6 +44,8 @@ def parse_args():
                     help="index into synthetic.CONFIGS for the main line (default 2: decode T=512)")
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--no-t4096", action="store_true", help="skip the T=4096 prefill case")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the standalone reduce and the MFMA probe")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens of the decode workload the oracle runs for the CPU baseline")
@@ -172,6 +174,103 @@ def summarize(r):
                 active_experts=nums["e_active"], block_m=r["block_m"], kernels=kernels)
 
 
+def _time_rotating(fn, inputs, steps, warmup):
+    """Average ms of fn(inp) over `steps` calls cycling through `inputs`
+    (copies whose total exceeds the 256 MB last-level cache, so every call
+    reads its rows from HBM)."""
+    import torch
+    for i in range(warmup):
+        fn(inputs[i % len(inputs)])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn(inputs[i % len(inputs)])
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / steps
+
+
+def time_reduce(steps, warmup, dev):
+    """The skewed workload's standalone moe_reduce_fused: expert_out [32768,
+    7168], 10 % of the slots masked, in bf16 and in the quantized form (FP8
+    E4M3 rows with a scale per row in, FP8 out with a scale per token). Bytes:
+    the valid rows read once, y written once, positions and weights (and the
+    scales) read once."""
+    import torch
+
+    import mixture_experts_routed_moe_amd as mr
+    import synthetic as S
+    cfg = S.CONFIGS[4]
+    T, K, H = cfg["T"], cfg["K"], cfg["H"]
+    d = S.make_reduce_inputs(T, K, H, dtype="bf16", seed=cfg["seed"], device=dev)
+    x, pos, w = d["expert_out"], d["token_topk_to_pos"], d["topk_weights"]
+    n_valid = int((pos >= 0).sum())
+    out = []
+
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    xs = [x, x.clone()]
+    ms = _time_rotating(lambda xi: mr.moe_reduce_fused(xi, pos, w, y=y), xs, steps, warmup)
+    nbytes = n_valid * H * 2 + T * H * 2 + T * K * 8
+    out.append(("skewed standalone reduce 4096x8x7168 bf16, 10% slots masked", ms, nbytes))
+    del xs, y
+
+    x8 = [x.to(torch.float8_e4m3fn) for _ in range(3)]
+    del x, d
+    g = torch.Generator().manual_seed(cfg["seed"] + 1)
+    x_sf = (torch.rand(T * K, generator=g) * 0.05 + 0.01).to(dev)
+    sf = (torch.rand(T, generator=g) * 4 + 1).to(dev)
+    y8 = torch.empty(T, H, dtype=torch.float8_e4m3fn, device=dev)
+    ms = _time_rotating(lambda xi: mr.moe_reduce_fused(xi, pos, w, y=y8, x_sf=x_sf, sf=sf), x8,
+                        steps, warmup)
+    nbytes = n_valid * H + T * H + T * K * 8 + n_valid * 4 + T * 4
+    out.append(("skewed standalone reduce 4096x8x7168 fp8 e4m3 + x_sf in, fp8 + sf out", ms,
+                nbytes))
+    res = []
+    for name, ms, nbytes in out:
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res.append({"workload": name, "ms": round(ms, 4), "algo_bytes": nbytes,
+                    "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    return res
+
+
+def mfma_probe(steps, warmup, dev):
+    """Labelled MFMA probe (not a workload of the metric): the gate/up and
+    down kernels on one expert receiving 4096 rows (T=4096, top-1, E=1,
+    d_hidden=7168, d_expert=2048): 16 row blocks of 256 share one expert's
+    weights, so the kernels run compute-bound at the prefill tile shapes."""
+    import torch
+
+    import mixture_experts_routed_moe_amd as mr
+    import synthetic as S
+    cfg = dict(name="mfma-probe", dtype="bf16", T=4096, H=7168, D=2048, E=1, K=1,
+               renorm=False, zipf=False, seed=7)
+    d = S.make_moe_inputs(cfg, device=dev)
+    tables = mr.moe_dispatch(d["topk_ids"], d["topk_weights"], 1, block_m=256)
+    ws, h, eo = mr.forward_workspace(tables, cfg["H"], cfg["D"], torch.bfloat16)
+    res = {}
+    for name, fn, flops in (
+            ("gate_up", lambda: mr.moe_expert_gate_up(d["x"], d["w_gate"], d["w_up"], tables, h=h),
+             4 * 4096 * 7168 * 2048),
+            ("down", lambda: mr.moe_expert_down(h, d["w_down"], tables, expert_out=eo),
+             2 * 4096 * 7168 * 2048)):
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "TFLOP_s": round(tf, 1),
+                     "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    res["workload"] = "MFMA probe: one expert, 4096 rows, 7168x2048 bf16, block_m 256"
+    return res
+
+
 def cpu_baseline(r, n_tokens):
     """The oracle (as it stands) on the first n_tokens tokens of the workload,
     plus its dispatch of the whole batch; time scaled to the whole layer."""
@@ -285,6 +384,14 @@ def main():
               % (S.CONFIGS[3]["name"], t4096["ms_per_layer"], t4096["TFLOP_s"],
                  t4096["HBM_GB_s"]), file=sys.stderr, flush=True)
 
+    extras = {}
+    if not args.no_extras:
+        extras["reduce_skewed"] = time_reduce(args.steps, args.warmup, dev)
+        torch.cuda.empty_cache()
+        extras["mfma_probe"] = mfma_probe(args.steps, args.warmup, dev)
+        torch.cuda.empty_cache()
+        print("# %s" % json.dumps(extras), file=sys.stderr, flush=True)
+
     gu = main_s["kernels"]["gate_up"]
     achieved = gu["GB_s"]
     traffic = counter_traffic()
@@ -311,6 +418,8 @@ def main():
                      "avg_launch_ms": gu["ms"]},
         "kernels": main_s["kernels"],
         "t4096": t4096,
+        "reduce_skewed": extras.get("reduce_skewed"),
+        "mfma_probe": extras.get("mfma_probe"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -61,7 +61,10 @@ typedef enum moe_status {
   MOE_ERR_HIP = 6          /* a launch failed (message from the HIP runtime)  */
 } moe_status;
 
-typedef enum moe_dtype { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2 } moe_dtype;
+/* Storage types. MOE_FP8_E4M3 is OCP FP8 E4M3 ("fn": no infinities, max
+ * 448), accepted by the reduce only; casts to it round to nearest even and
+ * saturate to +-448. */
+typedef enum moe_dtype { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2, MOE_FP8_E4M3 = 3 } moe_dtype;
 
 /*
  * Dispatch tables ([A] "forward" steps 2-5, [B] dispatch contract).
@@ -196,12 +199,30 @@ moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_u
  *   expert_out         [rows, H] of in_dtype;
  *   token_topk_to_pos  int32 [T, K], each value < rows;
  *   topk_weights       fp32 [T, K], or NULL for all-ones weights;
- *   y                  [T, H] of out_dtype (any of MOE_F16, MOE_BF16, MOE_F32).
+ *   in_dtype/out_dtype MOE_F16, MOE_BF16, MOE_F32 or MOE_FP8_E4M3;
+ *   y                  [T, H] of out_dtype.
  * Requires H % 256 == 0 ([C] section 2 lists H % 256 != 0 as an error case).
+ * A position >= rows is a precondition violation; the kernel skips it.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP. */
 moe_status moe_reduce_fused(const void* expert_out, int64_t rows,
                             const int32_t* token_topk_to_pos, const float* topk_weights, int T,
                             int K, int H, int in_dtype, int out_dtype, void* y, void* stream);
+
+/* The scaled / FP8 variants of the reduce ([C] section 1: the with_x_sf and
+ * with_sf switches and the FP8-output and quantized variants, one kernel):
+ *   y[t, :] = R_out( sf[t] * sum over k ascending with pos[t,k] >= 0 of
+ *                    (w[t,k] * x_sf[pos[t,k]]) * expert_out[pos[t,k], :] )
+ *   x_sf   fp32 [rows]: a scale per expanded row (per routed slot's row), one
+ *          multiply per slot; NULL = ones.
+ *   sf     fp32 [T]: a scale per token applied to the fp32 sum, one multiply
+ *          per output element; NULL = ones.
+ *   in_dtype / out_dtype: MOE_F16, MOE_BF16, MOE_F32 or MOE_FP8_E4M3
+ *          (e.g. FP8 rows with x_sf in, FP8 out with sf: the quantized form).
+ * Same requirements and errors as moe_reduce_fused. */
+moe_status moe_reduce_fused_scaled(const void* expert_out, int64_t rows,
+                                   const int32_t* token_topk_to_pos, const float* topk_weights,
+                                   const float* x_sf, const float* sf, int T, int K, int H,
+                                   int in_dtype, int out_dtype, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,12 +16,15 @@ import math
 import torch
 
 from ._lib import (MOE_BF16, MOE_ERR_DTYPE, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_F16, MOE_F32,
+                   MOE_FP8_E4M3,
                    MoeError, MoeTablesStruct, check, lib)
 
 __all__ = ["MoeError", "MoeTables", "default_block_m", "moe_dispatch", "moe_expert_gate_up",
            "moe_expert_down", "moe_routed_forward", "moe_reduce_fused", "forward_workspace"]
 
 _DTYPE_CODE = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
+# The reduce also reads and writes OCP FP8 E4M3 ("fn").
+_REDUCE_CODE = {**_DTYPE_CODE, torch.float8_e4m3fn: MOE_FP8_E4M3}
 
 _TABLE_FIELDS = {
     "group_sizes": ("E", torch.int32), "group_offsets": ("E", torch.int32),
@@ -208,11 +211,15 @@ def moe_routed_forward(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
     return y
 
 
-def moe_reduce_fused(expert_out, token_topk_to_pos, topk_weights=None, out_dtype=None, y=None):
-    """Step 3: y[t] = sum_k w[t,k] * expert_out[pos[t,k]] over pos >= 0, fp32
-    accumulation, one cast to out_dtype (default: expert_out's dtype)."""
+def moe_reduce_fused(expert_out, token_topk_to_pos, topk_weights=None, out_dtype=None, y=None,
+                     x_sf=None, sf=None):
+    """Step 3: y[t] = sf[t] * sum_k (w[t,k] * x_sf[pos[t,k]]) * expert_out[pos[t,k]]
+    over pos >= 0, fp32 accumulation, one cast to out_dtype (default:
+    expert_out's dtype). topk_weights, x_sf (fp32 [rows]) and sf (fp32 [T])
+    are optional (None = ones). expert_out and y may be float16, bfloat16,
+    float32 or float8_e4m3fn."""
     _check_tensor(expert_out, "expert_out", None, 2)
-    _require(expert_out.dtype in _DTYPE_CODE, MOE_ERR_DTYPE,
+    _require(expert_out.dtype in _REDUCE_CODE, MOE_ERR_DTYPE,
              "expert_out dtype %s not supported" % expert_out.dtype)
     dev = expert_out.device
     _check_tensor(token_topk_to_pos, "token_topk_to_pos", torch.int32, 2, dev)
@@ -223,13 +230,25 @@ def moe_reduce_fused(expert_out, token_topk_to_pos, topk_weights=None, out_dtype
         _require(tuple(topk_weights.shape) == (T, K), MOE_ERR_SHAPE,
                  "topk_weights shape %s != token_topk_to_pos shape %s"
                  % (tuple(topk_weights.shape), (T, K)))
+    if x_sf is not None:
+        _check_tensor(x_sf, "x_sf", torch.float32, 1, dev)
+        _require(x_sf.shape[0] == R, MOE_ERR_SHAPE, "x_sf must hold one scale per expert_out row")
+    if sf is not None:
+        _check_tensor(sf, "sf", torch.float32, 1, dev)
+        _require(sf.shape[0] == T, MOE_ERR_SHAPE, "sf must hold one scale per token")
     out_dtype = expert_out.dtype if out_dtype is None else out_dtype
-    _require(out_dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "out_dtype %s not supported" % out_dtype)
+    _require(out_dtype in _REDUCE_CODE, MOE_ERR_DTYPE, "out_dtype %s not supported" % out_dtype)
     if y is None:
         y = torch.empty(T, H, dtype=out_dtype, device=dev)
     _check_tensor(y, "y", out_dtype, 2, dev)
     _require(tuple(y.shape) == (T, H), MOE_ERR_SHAPE, "y must be [T, H]")
-    check(lib().moe_reduce_fused(_ptr(expert_out), R, _ptr(token_topk_to_pos), _ptr(topk_weights),
-                                 T, K, H, _DTYPE_CODE[expert_out.dtype], _DTYPE_CODE[out_dtype],
-                                 _ptr(y), _stream(dev)))
+    if x_sf is None and sf is None:
+        check(lib().moe_reduce_fused(_ptr(expert_out), R, _ptr(token_topk_to_pos),
+                                     _ptr(topk_weights), T, K, H, _REDUCE_CODE[expert_out.dtype],
+                                     _REDUCE_CODE[out_dtype], _ptr(y), _stream(dev)))
+    else:
+        check(lib().moe_reduce_fused_scaled(_ptr(expert_out), R, _ptr(token_topk_to_pos),
+                                            _ptr(topk_weights), _ptr(x_sf), _ptr(sf), T, K, H,
+                                            _REDUCE_CODE[expert_out.dtype],
+                                            _REDUCE_CODE[out_dtype], _ptr(y), _stream(dev)))
     return y

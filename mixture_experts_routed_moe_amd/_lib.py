@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_routed.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 4, 5, 6
-MOE_F16, MOE_BF16, MOE_F32 = 0, 1, 2
+MOE_F16, MOE_BF16, MOE_F32, MOE_FP8_E4M3 = 0, 1, 2, 3
 
 
 class MoeTablesStruct(ctypes.Structure):
@@ -73,6 +73,9 @@ def lib():
         L.moe_routed_forward.restype = i32
         L.moe_reduce_fused.argtypes = [vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_reduce_fused.restype = i32
+        L.moe_reduce_fused_scaled.argtypes = [vp, i64, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                              vp, vp]
+        L.moe_reduce_fused_scaled.restype = i32
         _lib = L
     return _lib
 

@@ -41,7 +41,7 @@ bool is_16bit(int dt) { return dt == MOE_F16 || dt == MOE_BF16; }
 
 bool is_float(int dt) { return is_16bit(dt) || dt == MOE_F32; }
 
-size_t dtype_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+size_t dtype_bytes(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_FP8_E4M3 ? 1 : 2); }
 
 moe_status check_table_sizes(int T, int K, int E, int block_m) {
   if (T < 1) return fail(MOE_ERR_SHAPE, "T must be >= 1 (got %d)", T);
@@ -257,14 +257,15 @@ moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_u
   err = moe::launch_down(down, *tables, st);
   if (err != hipSuccess) return hip_status(err, "moe_routed_forward down launch");
   const int64_t P = static_cast<int64_t>(tables->T) * tables->K;
-  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, tables->T,
-                           tables->K, H, dtype, dtype, y, st);
+  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
+                           nullptr, tables->T, tables->K, H, dtype, dtype, y, st);
   return hip_status(err, "moe_routed_forward reduce launch");
 }
 
-moe_status moe_reduce_fused(const void* expert_out, int64_t rows,
-                            const int32_t* token_topk_to_pos, const float* topk_weights, int T,
-                            int K, int H, int in_dtype, int out_dtype, void* y, void* stream) {
+moe_status moe_reduce_fused_scaled(const void* expert_out, int64_t rows,
+                                   const int32_t* token_topk_to_pos, const float* topk_weights,
+                                   const float* x_sf, const float* sf, int T, int K, int H,
+                                   int in_dtype, int out_dtype, void* y, void* stream) {
   if (!expert_out || !token_topk_to_pos || !y) {
     return fail(MOE_ERR_NULL, "expert_out, token_topk_to_pos and y must not be NULL");
   }
@@ -274,15 +275,25 @@ moe_status moe_reduce_fused(const void* expert_out, int64_t rows,
   if (H <= 0 || H % 256 != 0) {
     return fail(MOE_ERR_SHAPE, "H must be a positive multiple of 256 (got %d)", H);
   }
-  if (in_dtype < MOE_F16 || in_dtype > MOE_F32 || out_dtype < MOE_F16 || out_dtype > MOE_F32) {
-    return fail(MOE_ERR_DTYPE, "dtype codes must be MOE_F16, MOE_BF16 or MOE_F32");
+  if (in_dtype < MOE_F16 || in_dtype > MOE_FP8_E4M3 || out_dtype < MOE_F16 ||
+      out_dtype > MOE_FP8_E4M3) {
+    return fail(MOE_ERR_DTYPE,
+                "dtype codes must be MOE_F16, MOE_BF16, MOE_F32 or MOE_FP8_E4M3");
   }
-  if (static_cast<int64_t>(T) * (H / 256) > 0xffffffffLL) {
+  if (static_cast<int64_t>(T) * (H / 8) > 0xffffffffLL) {   // work-items of one launch
     return fail(MOE_ERR_SHAPE, "T * H too large for one launch");
   }
-  return hip_status(moe::launch_reduce(expert_out, rows, token_topk_to_pos, topk_weights, T, K, H,
-                                       in_dtype, out_dtype, y, static_cast<hipStream_t>(stream)),
+  return hip_status(moe::launch_reduce(expert_out, rows, token_topk_to_pos, topk_weights, x_sf,
+                                       sf, T, K, H, in_dtype, out_dtype, y,
+                                       static_cast<hipStream_t>(stream)),
                     "moe_reduce_fused launch");
+}
+
+moe_status moe_reduce_fused(const void* expert_out, int64_t rows,
+                            const int32_t* token_topk_to_pos, const float* topk_weights, int T,
+                            int K, int H, int in_dtype, int out_dtype, void* y, void* stream) {
+  return moe_reduce_fused_scaled(expert_out, rows, token_topk_to_pos, topk_weights, nullptr,
+                                 nullptr, T, K, H, in_dtype, out_dtype, y, stream);
 }
 
 }  // extern "C"

@@ -9,11 +9,14 @@ namespace moe {
 constexpr int kF16 = 0;
 constexpr int kBF16 = 1;
 constexpr int kF32 = 2;
+constexpr int kFP8 = 3;   // OCP FP8 E4M3 ("fn": no infinities, max 448)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_float(uint32_t b) {
   return __uint_as_float(b << 16);
@@ -34,6 +37,29 @@ __device__ __forceinline__ float f16_to_float(uint32_t b) {
 // fp32 -> binary16 with the hardware conversion (round to nearest even).
 __device__ __forceinline__ uint32_t float_to_f16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// fp32 -> FP8 E4M3 (OCP "fn"), round to nearest even, saturating to +-448
+// (infinities included); NaN -> 0x7f with the sign kept.
+__device__ __forceinline__ uint32_t float_to_fp8e4m3(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(f);
+  if (a != a) return sign | 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) {                       // below 2^-6: q * 2^-9, q in [0, 8]
+    return sign | static_cast<uint32_t>(rintf(a * 512.0f));
+  }
+  const uint32_t ua = __float_as_uint(a);
+  int e = static_cast<int>(ua >> 23) - 127;  // in [-6, 8]
+  uint32_t keep = (ua >> 20) & 7u;
+  const uint32_t rest = ua & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep += 1u;
+  if (keep == 8u) {
+    keep = 0u;
+    e += 1;
+  }
+  return sign | (static_cast<uint32_t>(e + 7) << 3) | keep;
 }
 
 template <int DT>

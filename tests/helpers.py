@@ -11,12 +11,15 @@ MAX_ABS_16 = 2e-2
 REL_L2_16 = 5e-3
 REL_L2_32 = 1e-4
 
-ORACLE_DT = {torch.float16: oracle.F16, torch.bfloat16: oracle.BF16, torch.float32: oracle.F32}
+ORACLE_DT = {torch.float16: oracle.F16, torch.bfloat16: oracle.BF16, torch.float32: oracle.F32,
+             torch.float8_e4m3fn: oracle.FP8}
 
 
 def storage(t):
-    """A torch tensor as the oracle's host storage (uint16 bits or float32)."""
+    """A torch tensor as the oracle's host storage (uint8 / uint16 bits or float32)."""
     t = t.detach().contiguous().cpu()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     if t.dtype in (torch.float16, torch.bfloat16):
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
