@@ -27,20 +27,27 @@
 //     about its order as long as A and B agree).
 //   * The A rows of the block (token rows of x gathered through
 //     sorted_token for gate/up; contiguous h rows for down) are shared by the
-//     4 waves through a double-buffered LDS tile (rows padded to 144 B so the
-//     MFMA fragment reads of 32 consecutive rows spread over the banks); one
-//     barrier per chunk.
-//   * Register double buffering: the loads of chunk c+1 are issued before
-//     the MFMAs of chunk c.
+//     4 waves through a double-buffered LDS tile; every A fragment read from
+//     LDS feeds two MFMAs. One barrier per chunk.
+//   * Software pipeline: the loads of chunk c+S-1 are issued while chunk c
+//     is multiplied (S-1 chunks of weights in flight).
 //   * Row groups of 32 rows with no valid row skip their MFMAs, so a block
-//     with 16 rows of a 32/64/128-row tile costs one row group of MFMA work.
+//     with 16 rows of a 32/64-row tile costs one row group of MFMA work.
 //   * Only blocks that hold rows are scheduled (the dispatch's active-block
 //     list), and they are mapped XCD-aware: workgroup L runs on XCD L % 8, so
 //     the natural tile order (active block major, column tile minor) is dealt
-//     out in equal contiguous ranges per XCD. The column tiles of one row block then share
-//     the A rows in that XCD's L2, and the blocks of one expert that spill
-//     into a second row block run at the same time on the same XCD, so their
-//     second read of the expert's weights is served by L2.
+//     out in equal contiguous ranges per XCD. The column tiles of one row
+//     block then share the A rows in that XCD's L2.
+// Two kernels share this design:
+//   * grouped_gemm_kernel, blocks of <= 64 rows (decode-sized groups): up to
+//     2 row groups of accumulators, A staged through registers and a padded
+//     LDS tile; small enough for two workgroups per CU.
+//   * grouped_gemm_wide_kernel, blocks of 128 or 256 rows (prefill-sized
+//     groups): up to 6 row groups (192 rows) in one pass over the weights,
+//     one workgroup per CU using all 512 registers of each wave, A rows in
+//     a swizzled LDS layout. A whole prefill-sized expert group then streams
+//     its weights once, where smaller blocks would stream them once per
+//     block.
 
 #include <type_traits>
 #include <utility>
@@ -54,25 +61,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunkK = 64;
 constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
-#ifndef MOE_STAGES_RG1
-#define MOE_STAGES_RG1 4
-#endif
-#ifndef MOE_STAGES_RG1_DOWN
-#define MOE_STAGES_RG1_DOWN 2
-#endif
-#ifndef MOE_STAGES_RG2
-#define MOE_STAGES_RG2 4
-#endif
 // Pipeline depths (chunks in flight), measured on MI355X: blocks of <= 32
 // rows stream gate/up best at depth 4 and down (half the bytes per column
-// tile, more workgroups) at depth 2.
-constexpr int kStagesRG1 = MOE_STAGES_RG1;
-constexpr int kStagesRG1Down = MOE_STAGES_RG1_DOWN;
-constexpr int kStagesRG2 = MOE_STAGES_RG2;   // 64-row blocks
-#ifndef MOE_STAGES_ROWSPLIT
-#define MOE_STAGES_ROWSPLIT 4
-#endif
-constexpr int kStagesRowSplit = MOE_STAGES_ROWSPLIT;
+// tile, more workgroups) at depth 2; 64-row blocks at depth 4. The wide
+// kernel runs at depth 4 (registers: 6 row groups of accumulators, the
+// weight ring and the A ring fill the 512 registers of one wave per SIMD).
+constexpr int kStagesRG1 = 4;
+constexpr int kStagesRG1Down = 2;
+constexpr int kStagesRG2 = 4;
+constexpr int kStagesWide = 4;
 
 struct GemmArgs {
   const uint16_t* a;
@@ -104,13 +101,9 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Weight loads: read once per block, so they are streamed past the caches.
+// Weight loads (a plain load: measured faster than the nontemporal form).
 __device__ __forceinline__ u32x4 load16_stream(const uint16_t* p) {
-#ifdef MOE_NT_B
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
   return *reinterpret_cast<const u32x4*>(p);
-#endif
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -274,11 +267,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   }
 
   const int nchunks = g.kd / kChunkK;
-#ifdef MOE_KROT
-  const int rot = (natural * 5) % nchunks;   // staggered start of the reduction walk
-#else
-  const int rot = 0;
-#endif
+  const int rot = 0;   // start of the reduction walk (chunk index rotation)
   const int a_seg = tid & 7;    // 16-byte segment of a 128-byte A row chunk
   const int a_row = tid >> 3;   // 0..31
 
@@ -300,121 +289,185 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     if (active == RG) {
       gemm_pass<DT, RG, RG, GATEUP, S>(g, lds_a, asrc, bptr, nchunks, rot, a_row, a_seg, lr, lh,
                                        out_row0, rows_pass, col0);
-    } else if constexpr (RG >= 2) {
-      if (active == 1) {
-        gemm_pass<DT, 1, RG, GATEUP, S>(g, lds_a, asrc, bptr, nchunks, rot, a_row, a_seg, lr, lh,
-                                        out_row0, rows_pass, col0);
-      } else if constexpr (RG >= 4) {
-        if (active == 2) {
-          gemm_pass<DT, 2, RG, GATEUP, S>(g, lds_a, asrc, bptr, nchunks, rot, a_row, a_seg, lr, lh,
-                                          out_row0, rows_pass, col0);
-        } else {
-          gemm_pass<DT, 3, RG, GATEUP, S>(g, lds_a, asrc, bptr, nchunks, rot, a_row, a_seg, lr,
-                                          lh, out_row0, rows_pass, col0);
-        }
-      }
+    } else if constexpr (RG == 2) {
+      gemm_pass<DT, 1, RG, GATEUP, S>(g, lds_a, asrc, bptr, nchunks, rot, a_row, a_seg, lr, lh,
+                                      out_row0, rows_pass, col0);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Row-split variant for large blocks (prefill-sized groups): NW waves, each
-// owning 32 rows of the block (a 128-row block uses 4 waves, a 256-row block
-// 8), so one workgroup covers a typical expert's rows and its weights stream
-// from HBM once. Each wave loads its own A rows straight into MFMA A-operand
-// registers; the workgroup's weight tile (128 weight rows: 64 columns of gate
-// and 64 of up, or 128 columns of down) is loaded once per chunk,
-// cooperatively, into a double-buffered LDS tile that all waves read. A wave
-// holds 4 accumulator tiles (64 registers). Same pipeline as above: chunk
-// c+S-1's A rows and weight share are loaded while chunk c is multiplied.
-template <int DT, bool GATEUP, int S, int NW, bool HAS_ROWS>
-__device__ __forceinline__ void rowsplit_pass(const GemmArgs& g,
-                                              uint16_t (*lds_b)[128][kLdsRow],
-                                              const uint16_t* a_ptr, const uint16_t* b_ptr,
-                                              int nchunks, int b_row, int b_seg, int lr, int lh,
-                                              int64_t out_row0, int rows_wave, int col_base) {
-  // The 16 KB weight tile of a chunk (128 rows x 128 B) is split over the
-  // 64*NW threads: kBVec 16-byte loads per thread.
-  constexpr int kBVec = 16 / NW;
-  f32x16 acc[4];
+// Wide-block kernel for blocks of 128 or 256 rows (prefill-sized groups): the
+// layout of grouped_gemm_kernel (4 waves, each owning 32 columns of gate and
+// of up, or 64 of down, for ALL rows of the block; weights streamed from HBM
+// straight into B-operand registers, so a block reads its expert's weights
+// once) with the block's A rows staged by direct-to-LDS loads
+// (global_load_lds_dwordx4) instead of through registers. That frees the
+// registers for up to NAMAX = 6 row groups of accumulators (192 rows: a
+// whole prefill-sized expert group in one pass) plus a deep weight ring, and
+// every A fragment read from LDS feeds two MFMAs.
+//
+// A stage holds the pass's rows as 8-row groups of 1 KB, one DMA instruction
+// each (lane L writes 16 bytes at L*16: row L/8 of the group, slot L%8).
+// Slot s of row r holds segment s ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2), so
+// the fragment reads of 16 consecutive rows at one segment touch 16
+// different (row parity, slot) pairs: distinct banks whether the LDS serves
+// 8 lanes x 16 B or 16 lanes x 16 B per clock. Row group q of a chunk (32
+// rows = 4 DMA groups) is loaded by the 4 waves, one group each.
+//
+// Pipeline: the loads of chunk c+S-1 (A by DMA, B into registers) are issued
+// while chunk c is multiplied, so S-1 chunks of weights are in flight (S = 6:
+// 160 KB per CU). Each step waits (vmcnt) for this wave's loads of chunk c,
+// then meets the other waves at a plain s_barrier (no fence: a workgroup
+// fence would wait for every DMA load in flight), and only then issues chunk
+// c+S-1 into the stage and register slot that chunk c-1 used, which every
+// wave finished reading before the barrier (its MFMAs consumed the reads).
+// S need not divide the chunk count: full groups of S steps run while every
+// step's prefetch exists, and the last S..2S-1 chunks run as a guarded tail.
+constexpr int kAGroupElems = 8 * kChunkK;   // one 8-row DMA group: 1 KB
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt / lgkmcnt at their maxima.
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most `after` chunks of `ops` loads each are outstanding
+// (s_waitcnt takes an immediate: one case per possible count).
+template <int OPS, int MAXAFTER>
+__device__ __forceinline__ void wait_chunks_after(int after) {
+  static_for<MAXAFTER + 1>([&](auto I) {
+    constexpr int k = decltype(I)::value;
+    if (after == k) wait_vmcnt<(k * OPS < 63 ? k * OPS : 63)>();
+  });
+}
+
+// Register-staged variant of wide_pass: the A share of chunk c+S-1 is loaded
+// into registers together with its weights (A first), and written to a
+// double-buffered LDS tile at the end of step c+S-2, one step before it is
+// multiplied. Since vector loads complete in issue order, waiting for an A
+// share never waits for the weights issued after it, so S-1 chunks of
+// weights stay in flight. Same LDS row layout as the DMA variant (this
+// thread writes the 16 bytes the DMA lane would have written).
+template <int DT, int NA, bool GATEUP, int S, int NAMAX>
+__device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
+                                          const uint16_t* const* a_src,
+                                          const uint16_t* const* bptr, int nchunks, int wave,
+                                          int lane, int lr, int lh, int64_t out_row0, int rows,
+                                          int col0) {
+  constexpr int kStage = NAMAX * 4 * kAGroupElems;
+  constexpr int kOps = NA + 8;   // vector memory ops per chunk per wave
+  f32x16 acc[NA][2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
-  u32x4 aring[S][4];
-  u32x4 bring[S][kBVec];
+  for (int q = 0; q < NA; ++q) {
+    acc[q][0] = f32x16{};
+    acc[q][1] = f32x16{};
+  }
+  u32x4 bring[S][2][4];
+  u32x4 aring[S][NA];
 
   auto load_chunk = [&](int c, int slot) {
     const int64_t off = static_cast<int64_t>(c) * kChunkK;
-    if constexpr (HAS_ROWS) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) aring[slot][t] = load16(a_ptr + off + t * 8);
+    for (int q = 0; q < NA; ++q) aring[slot][q] = load16(a_src[q] + off);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bring[slot][j][t] = load16_stream(bptr[j] + off + t * 8);
     }
-#pragma unroll
-    for (int t = 0; t < kBVec; ++t) bring[slot][t] = load16(b_ptr + off + t * 8);
   };
-  auto stage_b = [&](int slot, int buf) {
+  // Write chunk c's A share (ring slot `slot`) into LDS buffer c % 2.
+  auto stage_a = [&](int c, int slot) {
+    uint16_t* stage = lds_ring + (c & 1) * kStage + wave * kAGroupElems + lane * 8;
 #pragma unroll
-    for (int t = 0; t < kBVec; ++t) {
-      *reinterpret_cast<u32x4*>(&lds_b[buf][b_row][b_seg * kBVec * 8 + t * 8]) = bring[slot][t];
+    for (int q = 0; q < NA; ++q) {
+      *reinterpret_cast<u32x4*>(stage + q * 4 * kAGroupElems) = aring[slot][q];
     }
   };
 
+  const int f_row = (lr & 7) ^ ((lr >> 3) & 1);
+  const int row_off = (lr >> 3) * kAGroupElems + (lr & 7) * kChunkK;
+  auto multiply = [&](int c, auto U) {
+    constexpr int u = decltype(U)::value % S;
+    const uint16_t* stage = lds_ring + (c & 1) * kStage + row_off;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int slot = (lh * 4 + t) ^ f_row;
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(stage + q * 4 * kAGroupElems + slot * 8);
+        acc[q][0] = mfma32x32x16<DT>(a, bring[u][0][t], acc[q][0]);
+        acc[q][1] = mfma32x32x16<DT>(a, bring[u][1][t], acc[q][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Prologue: chunks 0..S-2 in flight; stage chunk 0's A share.
 #pragma unroll
   for (int st = 0; st < S - 1; ++st) load_chunk(st, st);
-  stage_b(0, 0);
-  __syncthreads();
+  wait_vmcnt<(8 + (S - 2) * kOps < 63 ? 8 + (S - 2) * kOps : 63)>();
+  stage_a(0, 0);
 
-  auto step = [&](int c, auto U, auto PREFETCH, auto STAGE) {
+  // Step c: wait for chunk c's weights, barrier (chunk c's A share is in
+  // LDS; every wave is done with buffer (c+1) % 2), prefetch chunk c+S-1,
+  // multiply chunk c, then wait for chunk c+1's A share and stage it.
+  int c0 = 0;
+  for (; c0 + 2 * S - 1 <= nchunks - 1; c0 += S) {
+    static_for<S>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      wait_vmcnt<(S - 2) * kOps>();
+      __builtin_amdgcn_s_barrier();
+      load_chunk(c0 + u + S - 1, (u + S - 1) % S);
+      multiply(c0 + u, U);
+      wait_vmcnt<(8 + (S - 2) * kOps < 63 ? 8 + (S - 2) * kOps : 63)>();
+      stage_a(c0 + u + 1, (u + 1) % S);
+    });
+  }
+  // Tail: the last R chunks, S <= R < 2S.
+  const int rem = nchunks - c0;
+  static_for<2 * S>([&](auto U) {
     constexpr int u = decltype(U)::value;
-    if constexpr (decltype(PREFETCH)::value) load_chunk(c + S - 1, (u + S - 1) % S);
-    constexpr int buf = u & 1;
-    if constexpr (HAS_ROWS) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 b =
-              *reinterpret_cast<const u32x4*>(&lds_b[buf][j * 32 + lr][lh * 32 + t * 8]);
-          acc[j] = mfma32x32x16<DT>(aring[u][t], b, acc[j]);
-        }
+    if (u < rem) {
+      wait_chunks_after<kOps, S - 2>(min(S - 2, rem - 1 - u));
+      __builtin_amdgcn_s_barrier();
+      if (u + S - 1 < rem) load_chunk(c0 + u + S - 1, (u + S - 1) % S);
+      multiply(c0 + u, U);
+      if (u + 1 < rem) {
+        // Chunks issued after chunk c+1: up to min(c+S-1, n-1).
+        const int after = min(S - 2, rem - 2 - u);
+        static_for<S - 1>([&](auto I) {
+          constexpr int k = decltype(I)::value;
+          if (after == k) wait_vmcnt<(8 + k * kOps < 63 ? 8 + k * kOps : 63)>();
+        });
+        stage_a(c0 + u + 1, (u + 1) % S);
       }
     }
-    if constexpr (decltype(STAGE)::value) stage_b((u + 1) % S, buf ^ 1);
-    __syncthreads();
-  };
-  int c0 = 0;
-  for (; c0 + S < nchunks; c0 += S) {
-    static_for<S>([&](auto U) { step(c0 + U, U, std::true_type{}, std::true_type{}); });
-  }
-  static_for<S>([&](auto U) {
-    step(c0 + U, U, std::bool_constant<decltype(U)::value == 0>{},
-         std::bool_constant<(decltype(U)::value < S - 1)>{});
   });
 
-  if constexpr (HAS_ROWS) {
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = (i >> 2) * 8 + lh * 4 + (i & 3);
-      if (row < rows_wave) {
-        uint16_t* out = g.c + (out_row0 + row) * g.n + col_base + lr;
+      const int row = q * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+      if (row < rows) {
+        uint16_t* out = g.c + (out_row0 + row) * g.n + col0 + lr;
         if constexpr (GATEUP) {
-          out[0] = static_cast<uint16_t>(from_float<DT>(silu(acc[0][i]) * acc[2][i]));
-          out[32] = static_cast<uint16_t>(from_float<DT>(silu(acc[1][i]) * acc[3][i]));
+          out[0] = static_cast<uint16_t>(from_float<DT>(silu(acc[q][0][i]) * acc[q][1][i]));
         } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            out[32 * j] = static_cast<uint16_t>(from_float<DT>(acc[j][i]));
-          }
+          out[0] = static_cast<uint16_t>(from_float<DT>(acc[q][0][i]));
+          out[32] = static_cast<uint16_t>(from_float<DT>(acc[q][1][i]));
         }
       }
     }
   }
 }
 
-template <int DT, bool GATEUP, int S, int NW>
-__global__ __launch_bounds__(64 * NW) void grouped_gemm_rowsplit_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][128][kLdsRow];
-  constexpr int kSegs = NW / 2;           // threads per 128-byte weight-row chunk
-  constexpr int kBVec = 16 / NW;          // 16-byte loads per thread
+template <int DT, bool GATEUP, int S, int NAMAX>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_ring[2 * NAMAX * 4 * kAGroupElems];
 
   const int total = g.active_count[0] * g.n_tiles;
   const int per_xcd = (total + 7) >> 3;
@@ -438,44 +491,66 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_rowsplit_kernel(GemmArgs
   const int64_t kd = g.kd;
   const int nchunks = g.kd / kChunkK;
 
-  // This thread's share of the weight tile: row b_row of 128, segment b_seg.
-  const int b_row = tid / kSegs;
-  const int b_seg = tid % kSegs;
-  const int col_base = nt * (GATEUP ? 64 : 128);
-  const uint16_t* b_ptr;
+  const int64_t expert_row0 = static_cast<int64_t>(e) * g.n;
+  int col0;
+  const uint16_t* bptr[2];
   if constexpr (GATEUP) {
-    const uint16_t* w = b_row < 64 ? g.b0 : g.b1;
-    b_ptr = w + (static_cast<int64_t>(e) * g.n + col_base + (b_row & 63)) * kd +
-            b_seg * kBVec * 8;
+    col0 = nt * 128 + wave * 32;
+    bptr[0] = g.b0 + (expert_row0 + col0 + lr) * kd + lh * 32;
+    bptr[1] = g.b1 + (expert_row0 + col0 + lr) * kd + lh * 32;
   } else {
-    b_ptr = g.b0 + (static_cast<int64_t>(e) * g.n + col_base + b_row) * kd + b_seg * kBVec * 8;
+    col0 = nt * 256 + wave * 64;
+    bptr[0] = g.b0 + (expert_row0 + col0 + lr) * kd + lh * 32;
+    bptr[1] = g.b0 + (expert_row0 + col0 + 32 + lr) * kd + lh * 32;
   }
 
-  for (int r0 = 0; r0 < rows; r0 += 32 * NW) {
-    const int rows_wave = min(32, rows - r0 - wave * 32);   // may be <= 0
-    int r = wave * 32 + lr;
-    if (r >= rows - r0) r = 0;                                // in bounds, never stored
-    const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
-    const uint16_t* a_ptr = g.a + src * kd + lh * 32;
-    const int64_t out_row0 = m_start + r0 + wave * 32;
-    if (rows_wave > 0) {
-      rowsplit_pass<DT, GATEUP, S, NW, true>(g, lds_b, a_ptr, b_ptr, nchunks, b_row, b_seg, lr,
-                                             lh, out_row0, rows_wave, col_base);
-    } else {
-      rowsplit_pass<DT, GATEUP, S, NW, false>(g, lds_b, a_ptr, b_ptr, nchunks, b_row, b_seg, lr,
-                                              lh, out_row0, rows_wave, col_base);
+  // One pass over the weights covers up to NAMAX row groups; a block with
+  // more rows (at most 8 groups) takes two balanced passes of up to 4 groups
+  // (written out rather than as a loop, so the register allocation of the
+  // large pass is not burdened by the loop).
+  auto run_pass = [&](int r0, auto NAP) {
+    constexpr int kMaxNa = decltype(NAP)::value;
+    const int rows_pass = min(32 * kMaxNa, rows - r0);
+    // This lane's DMA source for row group q: row 32q + 8*wave + lane/8 of
+    // the pass (row 0 of the pass past its rows: in bounds, never stored),
+    // segment (lane % 8) ^ f(row) with f(row) = (lane / 8) ^ (wave % 2).
+    const uint16_t* a_src[kMaxNa];
+    const int seg = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+#pragma unroll
+    for (int q = 0; q < kMaxNa; ++q) {
+      int r = 32 * q + 8 * wave + (lane >> 3);
+      if (r >= rows_pass) r = 0;
+      const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
+      a_src[q] = g.a + src * kd + seg * 8;
     }
+    const int active = (rows_pass + 31) >> 5;
+    static_for<kMaxNa>([&](auto I) {
+      constexpr int na = decltype(I)::value + 1;
+      if (active == na) {
+        wide_pass<DT, na, GATEUP, S, NAMAX>(g, lds_ring, a_src, bptr, nchunks, wave, lane, lr,
+                                            lh, m_start + r0, rows_pass, col0);
+      }
+    });
+  };
+  if (rows <= 32 * NAMAX) {
+    run_pass(0, int_c<NAMAX>{});
+  } else {
+    run_pass(0, int_c<4>{});
+    __builtin_amdgcn_s_barrier();   // every wave is done with the LDS tile
+    run_pass(128, int_c<4>{});
   }
 }
 
-template <int DT, bool GATEUP, int NW>
-void launch_rowsplit(unsigned grid, const GemmArgs& g, hipStream_t stream) {
-  if ((g.kd / kChunkK) % kStagesRowSplit == 0) {
-    hipLaunchKernelGGL((grouped_gemm_rowsplit_kernel<DT, GATEUP, kStagesRowSplit, NW>),
-                       dim3(grid), dim3(64 * NW), 0, stream, g);
+template <int DT, bool GATEUP, int NAMAX>
+void launch_wide(unsigned grid, const GemmArgs& g, hipStream_t stream) {
+  // Depth 4 needs at least 4 chunks (kd >= 256); a 128-long reduction (the
+  // shortest the shape rules allow: 2 chunks) runs at depth 2.
+  if (g.kd / kChunkK >= kStagesWide) {
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<DT, GATEUP, kStagesWide, NAMAX>), dim3(grid),
+                       dim3(kThreads), 0, stream, g);
   } else {
-    hipLaunchKernelGGL((grouped_gemm_rowsplit_kernel<DT, GATEUP, 2, NW>), dim3(grid),
-                       dim3(64 * NW), 0, stream, g);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<DT, GATEUP, 2, NAMAX>), dim3(grid),
+                       dim3(kThreads), 0, stream, g);
   }
 }
 
@@ -509,22 +584,20 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
   g.n = p.n;
   g.kd = p.kd;
   g.block_m = t.block_m;
-  const bool rowsplit = t.block_m >= 128;
-  g.n_tiles = p.n / (rowsplit ? (GATEUP ? 64 : 128) : (GATEUP ? 128 : 256));
+  // Blocks of <= 64 rows: grouped_gemm_kernel (128 h columns or 256 output
+  // columns per workgroup); 128- and 256-row blocks: the wide kernel (same
+  // column tiles).
+  g.n_tiles = p.n / (GATEUP ? 128 : 256);
   const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
   const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
-  if (rowsplit) {
-    if (t.block_m == 128) {
-      launch_rowsplit<DT, GATEUP, 4>(grid, g, stream);
-    } else {
-      launch_rowsplit<DT, GATEUP, 8>(grid, g, stream);
-    }
-    return hipGetLastError();
-  }
   if (t.block_m <= 32) {
     launch_rg<DT, 1, GATEUP, GATEUP ? kStagesRG1 : kStagesRG1Down>(grid, g, stream);
-  } else {
+  } else if (t.block_m == 64) {
     launch_rg<DT, 2, GATEUP, kStagesRG2>(grid, g, stream);
+  } else if (t.block_m == 128) {
+    launch_wide<DT, GATEUP, 4>(grid, g, stream);
+  } else {
+    launch_wide<DT, GATEUP, 6>(grid, g, stream);
   }
   return hipGetLastError();
 }

@@ -117,6 +117,21 @@ def test_forward_ragged(dtype, block_m):
     _check_pairs(tables, h, eo, hp, ep, 3)
 
 
+@pytest.mark.parametrize("block_m", [128, 256])
+def test_forward_wide_blocks(block_m):
+    """Prefill-sized blocks: full 256-row blocks (two passes of 4 row groups),
+    a 193..224-row tail block, one-pass blocks of up to 6 row groups, and
+    reductions of 8 and 6 chunks (the pipeline tail with and without a full
+    group of steps)."""
+    d = _custom(T=600, H=512, D=384, E=4, K=2, dtype="bf16", seed=21, mask=0.05, hot=1)
+    tables, h, eo, y = _run(d, block_m=block_m)
+    sizes = tables.group_sizes.cpu().numpy()
+    assert sizes.max() > 2 * 256 and (sizes % 256).max() > 0
+    y_ref, hp, ep = _oracle(d)
+    assert_close_16(y.float().cpu().numpy(), y_ref, "wide blocks")
+    _check_pairs(tables, h, eo, hp, ep, 2)
+
+
 def test_forward_empty_experts_and_all_masked_tokens():
     d = _custom(T=40, H=256, D=128, E=16, K=2, dtype="bf16", seed=12)
     ids = d["topk_ids"]
