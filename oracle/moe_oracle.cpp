@@ -416,4 +416,62 @@ int oracle_reduce(int dt, const void* X, int64_t R, const int32_t* pos, const fl
   return oracle_reduce_scaled(dt, X, R, pos, w, nullptr, nullptr, T, K, H, y);
 }
 
+// ---------------------------------------------------------------- router --
+// The gate in front of the routed experts, as the workload recipes of the
+// routed-MoE benchmark state it: router weights Wr [E, H] in fp32, scores =
+// fp32 softmax of the logits x . Wr^T, the top-k experts by score with ties
+// going to the lower expert index, routing weights = the selected scores,
+// optionally renormalised to sum to 1 over the k selected experts.
+//   logits[t, e] = fp32 fused multiply-add chain over h = 0..H-1 ascending of
+//                  x[t, h] * Wr[e, h] (x widened exactly from its dtype);
+//   selection:     k rounds, each taking the largest remaining logit (the
+//                  softmax is strictly increasing, so ranking by logit is
+//                  ranking by score), ties to the lower index;
+//   scores:        m = the largest logit, Z = sum over e ascending of
+//                  expf(logit_e - m), p_e = expf(logit_e - m) / Z;
+//   weights:       p of the selected experts in selection order; with
+//                  renorm, each divided by their sum (k ascending).
+// Inputs must be finite. Writes logits [T, E], ids [T, K], w [T, K].
+int oracle_gate(int dt, const void* x, const float* wr, int T, int H, int E, int K, int renorm,
+                float* logits, int32_t* ids, float* w) {
+  if (!(dt == kF16 || dt == kBF16 || dt == kF32) || T < 0 || H <= 0 || E <= 0 || K <= 0 ||
+      K > E) {
+    return -1;
+  }
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    std::vector<float> xt(H);
+    for (int h = 0; h < H; ++h) xt[h] = load_elem(dt, x, static_cast<int64_t>(t) * H + h);
+    float* lt = logits + static_cast<int64_t>(t) * E;
+    for (int e = 0; e < E; ++e) {
+      const float* we = wr + static_cast<int64_t>(e) * H;
+      float acc = 0.0f;
+      for (int h = 0; h < H; ++h) acc = std::fma(xt[h], we[h], acc);
+      lt[e] = acc;
+    }
+    std::vector<char> taken(E, 0);
+    int32_t* it = ids + static_cast<int64_t>(t) * K;
+    for (int k = 0; k < K; ++k) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || lt[e] > lt[best]) best = e;   // strict: ties keep the lower index
+      }
+      taken[best] = 1;
+      it[k] = best;
+    }
+    const float m = lt[it[0]];
+    float z = 0.0f;
+    for (int e = 0; e < E; ++e) z += std::exp(lt[e] - m);
+    float* wt = w + static_cast<int64_t>(t) * K;
+    for (int k = 0; k < K; ++k) wt[k] = std::exp(lt[it[k]] - m) / z;
+    if (renorm) {
+      float s = 0.0f;
+      for (int k = 0; k < K; ++k) s += wt[k];
+      for (int k = 0; k < K; ++k) wt[k] = wt[k] / s;
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"
