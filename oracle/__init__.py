@@ -45,7 +45,7 @@ def lib():
         L.oracle_reduce.argtypes = [i32, vp, i64, i32p, f32p, i32, i32, i32, f32p]
         L.oracle_reduce_scaled.argtypes = [i32, vp, i64, i32p, f32p, f32p, f32p, i32, i32, i32,
                                            f32p]
-        L.oracle_gate.argtypes = [i32, vp, f32p, i32, i32, i32, i32, i32, f32p, i32p, f32p]
+        L.oracle_gate.argtypes = [i32, vp, f32p, f32p, i32, i32, i32, i32, i32, f32p, i32p, f32p]
         _lib = L
     return _lib
 
@@ -186,11 +186,12 @@ def reduce(dt, X, pos, w=None, x_sf=None, sf=None):
     return y
 
 
-def gate(dt, x, wr, K, renorm):
-    """oracle_gate: router logits (fp32 fma chain, h ascending), top-K by
-    logit (ties to the lower index), softmax scores, optional renormalisation.
-    x: [T, H] storage of dtype dt; wr: [E, H] float32. Returns dict of
-    logits [T, E] float32, ids [T, K] int32, weights [T, K] float32."""
+def gate(dt, x, wr, K, renorm, bias=None):
+    """oracle_gate: router logits (fp32 fma chain, h ascending, plus an
+    optional per-expert bias), top-K by logit (ties to the lower index),
+    softmax scores, optional renormalisation. x: [T, H] storage of dtype dt;
+    wr: [E, H] float32; bias: [E] float32 or None. Returns dict of logits
+    [T, E] float32, ids [T, K] int32, weights [T, K] float32."""
     xs = _storage(np.asarray(x), dt)
     T, H = xs.shape
     wr = _c(wr, np.float32)
@@ -199,7 +200,9 @@ def gate(dt, x, wr, K, renorm):
     logits = np.empty((T, E), np.float32)
     ids = np.empty((T, K), np.int32)
     w = np.empty((T, K), np.float32)
-    rc = lib().oracle_gate(dt, _ptr(xs), _ptr(wr), T, H, E, K, int(bool(renorm)), _ptr(logits),
-                           _ptr(ids), _ptr(w))
+    b = None if bias is None else _c(bias, np.float32)
+    assert b is None or b.shape == (E,)
+    rc = lib().oracle_gate(dt, _ptr(xs), _ptr(wr), _ptr(b), T, H, E, K, int(bool(renorm)),
+                           _ptr(logits), _ptr(ids), _ptr(w))
     assert rc == 0, "oracle_gate rejected its arguments"
     return dict(logits=logits, ids=ids, weights=w)

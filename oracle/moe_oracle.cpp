@@ -423,7 +423,9 @@ int oracle_reduce(int dt, const void* X, int64_t R, const int32_t* pos, const fl
 // going to the lower expert index, routing weights = the selected scores,
 // optionally renormalised to sum to 1 over the k selected experts.
 //   logits[t, e] = fp32 fused multiply-add chain over h = 0..H-1 ascending of
-//                  x[t, h] * Wr[e, h] (x widened exactly from its dtype);
+//                  x[t, h] * Wr[e, h] (x widened exactly from its dtype), plus
+//                  bias[e] in one fp32 addition when a bias is given (the
+//                  skewed workload adds 2*log(1/rank) to the logits);
 //   selection:     k rounds, each taking the largest remaining logit (the
 //                  softmax is strictly increasing, so ranking by logit is
 //                  ranking by score), ties to the lower index;
@@ -432,8 +434,8 @@ int oracle_reduce(int dt, const void* X, int64_t R, const int32_t* pos, const fl
 //   weights:       p of the selected experts in selection order; with
 //                  renorm, each divided by their sum (k ascending).
 // Inputs must be finite. Writes logits [T, E], ids [T, K], w [T, K].
-int oracle_gate(int dt, const void* x, const float* wr, int T, int H, int E, int K, int renorm,
-                float* logits, int32_t* ids, float* w) {
+int oracle_gate(int dt, const void* x, const float* wr, const float* bias, int T, int H, int E,
+                int K, int renorm, float* logits, int32_t* ids, float* w) {
   if (!(dt == kF16 || dt == kBF16 || dt == kF32) || T < 0 || H <= 0 || E <= 0 || K <= 0 ||
       K > E) {
     return -1;
@@ -447,7 +449,7 @@ int oracle_gate(int dt, const void* x, const float* wr, int T, int H, int E, int
       const float* we = wr + static_cast<int64_t>(e) * H;
       float acc = 0.0f;
       for (int h = 0; h < H; ++h) acc = std::fma(xt[h], we[h], acc);
-      lt[e] = acc;
+      lt[e] = bias ? acc + bias[e] : acc;
     }
     std::vector<char> taken(E, 0);
     int32_t* it = ids + static_cast<int64_t>(t) * K;

@@ -12,8 +12,10 @@ renormalised. What pins the oracle, independently of its own code:
   * scores equal to a float64 softmax of its logits; K = E without
     renormalisation sums to 1; renormalised weights sum to 1; the two-expert
     case is the logistic function of the logit difference;
+  * a logit bias adds in one fp32 addition (logits = unbiased + bias);
   * agreement with the workload recipe's own router (float64 logits, torch
-    softmax and sort) except at near-ties of the logits.
+    softmax and sort) except at near-ties of the logits, including the
+    skewed recipe's Zipf bias.
 """
 import numpy as np
 import pytest
@@ -121,22 +123,44 @@ def test_gate_two_experts_is_logistic():
     assert np.allclose(g["weights"][:, 0], np.maximum(p0, 1 - p0), rtol=2e-6, atol=0)
 
 
-@pytest.mark.parametrize("ci", [0, 1])
-def test_gate_matches_workload_recipe_router(ci):
+def test_gate_bias_adds_once():
+    rng = np.random.default_rng(6)
+    T, H, E = 8, 128, 16
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    b = (rng.standard_normal(E) * 3).astype(np.float32)
+    g0 = oracle.gate(oracle.F32, x, wr, K=4, renorm=True)
+    g1 = oracle.gate(oracle.F32, x, wr, K=4, renorm=True, bias=b)
+    assert np.array_equal(g1["logits"], (g0["logits"] + b[None, :]).astype(np.float32))
+    assert np.array_equal(g1["ids"], _stable_topk(g1["logits"], 4))
+
+
+@pytest.mark.parametrize("ci,T", [(0, None), (1, None), (4, 256)])
+def test_gate_matches_workload_recipe_router(ci, T):
     cfg = S.CONFIGS[ci]
-    d = S.make_moe_inputs(cfg, device="cpu", weights=False)
+    d = S.make_moe_inputs(cfg, device="cpu", weights=False, T=T)
+    T = d["T"]
     x = d["x"]
     dt = {torch.float16: oracle.F16, torch.bfloat16: oracle.BF16}[x.dtype]
     xs = x.contiguous().view(torch.int16).numpy().view(np.uint16)
-    g = oracle.gate(dt, xs, d["router"].numpy(), K=cfg["K"], renorm=cfg["renorm"])
+    bias = S.zipf_bias(cfg["E"]).numpy() if cfg.get("zipf") else None
+    g = oracle.gate(dt, xs, d["router"].numpy(), K=cfg["K"], renorm=cfg["renorm"], bias=bias)
     ids_ref = d["topk_ids"].numpy()
-    l64 = x.to(torch.float64) @ d["router"].to(torch.float64).t()
+    l64 = (x.to(torch.float64) @ d["router"].to(torch.float64).t()).numpy()
+    if bias is not None:
+        l64 = l64 + bias.astype(np.float64)
     bad = np.where((g["ids"] != ids_ref).any(axis=1))[0]
     # the recipe ranks float64 logits; the oracle ranks fp32 fma-chain logits:
     # they may only disagree where two candidates' logits are within rounding
-    assert len(bad) <= max(1, cfg["T"] // 100)
+    assert len(bad) <= max(1, T // 100)
     for t in bad:
-        l = np.sort(l64[t].numpy())[::-1][: cfg["K"] + 1]
+        l = np.sort(l64[t])[::-1][: cfg["K"] + 1]
         assert np.min(np.abs(np.diff(l))) < 1e-5
-    ok = np.setdiff1d(np.arange(cfg["T"]), bad)
-    assert np.allclose(g["weights"][ok], d["topk_weights"].numpy()[ok], rtol=1e-5, atol=1e-7)
+    ok = np.setdiff1d(np.arange(T), bad)
+    # weights: exp turns a logit difference dl into a relative weight
+    # difference of about dl; the fp32 chain is within H*2^-24*sum|x w| of
+    # the float64 logit, and w = exp(l_k - m) / Z involves three logits.
+    xa = np.abs(x.to(torch.float64).numpy())
+    dl = cfg["H"] * 2.0 ** -24 * (xa @ np.abs(d["router"].numpy().astype(np.float64)).T)
+    rtol = 3 * dl.max() + 2e-6
+    assert np.allclose(g["weights"][ok], d["topk_weights"].numpy()[ok], rtol=rtol, atol=1e-9)
