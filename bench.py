@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pmc_grouped_gemm_gate_up_deepseek_decode.md")
 GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", f)
                 for f in ("grouped_gemm.hip", "common.hpp")]
@@ -271,6 +272,47 @@ def mfma_probe(steps, warmup, dev):
     return res
 
 
+def time_gate(steps, warmup, dev):
+    """The router gate (moe_gate) at the decode and prefill shapes: logits
+    [T, 256] from x [T, 7168] and an fp32 router [256, 7168], top-8, softmax,
+    renormalised. An fp32 vector-ALU kernel (one fma chain per logit): FLOPs
+    2*T*E*H against the fp32 vector peak; bytes x + router + logits + ids +
+    weights."""
+    import torch
+
+    import mixture_experts_routed_moe_amd as mr
+    import synthetic as S
+    res = []
+    for ci in (2, 3):
+        cfg = S.CONFIGS[ci]
+        d = S.make_moe_inputs(cfg, device=dev, weights=False)
+        T, H, E, K = cfg["T"], cfg["H"], cfg["E"], cfg["K"]
+        out = (torch.empty(T, K, dtype=torch.int32, device=dev),
+               torch.empty(T, K, dtype=torch.float32, device=dev),
+               torch.empty(T, E, dtype=torch.float32, device=dev))
+        fn = lambda: mr.moe_gate(d["x"], d["router"], K, renorm=cfg["renorm"], out=out)
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        flops = 2.0 * T * E * H
+        nbytes = T * H * 2 + E * H * 4 + T * E * 4 + T * K * 8
+        tf = flops / (ms * 1e-3) / 1e12
+        res.append({"workload": "router gate, %s (T=%d, E=%d, H=%d, top-%d)" % (cfg["name"], T, E,
+                                                                               H, K),
+                    "us": round(ms * 1e3, 2), "TFLOP_s": round(tf, 2),
+                    "fp32_vector_frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                    "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+        del d
+    return res
+
+
 def cpu_baseline(r, n_tokens):
     """The oracle (as it stands) on the first n_tokens tokens of the workload,
     plus its dispatch of the whole batch; time scaled to the whole layer."""
@@ -390,6 +432,8 @@ def main():
         torch.cuda.empty_cache()
         extras["mfma_probe"] = mfma_probe(args.steps, args.warmup, dev)
         torch.cuda.empty_cache()
+        extras["gate"] = time_gate(args.steps, args.warmup, dev)
+        torch.cuda.empty_cache()
         print("# %s" % json.dumps(extras), file=sys.stderr, flush=True)
 
     gu = main_s["kernels"]["gate_up"]
@@ -420,6 +464,7 @@ def main():
         "t4096": t4096,
         "reduce_skewed": extras.get("reduce_skewed"),
         "mfma_probe": extras.get("mfma_probe"),
+        "gate": extras.get("gate"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

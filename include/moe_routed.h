@@ -8,6 +8,8 @@
  *     y[t] = sum_k w_k * Down_{e_k}( SiLU(Gate_{e_k} x_t) * Up_{e_k} x_t )
  *
  * in three steps, each a call of this library:
+ *   0. moe_gate             -- (in front of the path) router logits, top-k
+ *                              ids and routing weights on the device;
  *   1. moe_dispatch         -- expert-sorted dispatch tables;
  *   2. moe_expert_gate_up   -- grouped GEMM over the stacked gate/up weights
  *                              with SiLU(gate)*up fused in the epilogue,
@@ -116,6 +118,30 @@ typedef struct moe_tables {
   int32_t *chunk_flags;  /* [num_chunks]     */
   int32_t *pair_rank;    /* [P]              */
 } moe_tables;
+
+/* Step 0 (in front of the path): the router gate. The routed-MoE workload
+ * recipes define it: router weights Wr [E, H] in fp32, fp32 softmax of the
+ * logits x . Wr^T, the top-k experts by score with ties to the lower expert
+ * index, routing weights = the selected scores, renormalised to sum to 1
+ * where asked; the skewed workload adds a per-expert bias to the logits.
+ *   x             [T, H] of dtype (MOE_F16, MOE_BF16 or MOE_F32);
+ *   w_router      fp32 [E, H];
+ *   bias          fp32 [E] added to every token's logits, or NULL;
+ *   logits        fp32 [T, E] output: logits[t, e] = (one fp32 fused
+ *                 multiply-add chain over h = 0..H-1 ascending of
+ *                 x[t, h] * w_router[e, h]) + bias[e] -- reproducible bit
+ *                 for bit under that definition;
+ *   topk_ids      int32 [T, K] output: the K largest logits of each token
+ *                 in descending order, ties to the lower index (ranking by
+ *                 logit is ranking by score: the softmax is increasing);
+ *   topk_weights  fp32 [T, K] output: softmax(logits[t])[topk_ids[t, k]],
+ *                 divided by their sum over k when renorm != 0.
+ * The outputs feed moe_dispatch directly. Inputs must be finite.
+ * Requires H % 64 == 0, 1 <= E <= 1024, 1 <= K <= min(E, 64), T >= 0.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP. */
+moe_status moe_gate(const void* x, const float* w_router, const float* bias, int T, int H, int E,
+                    int K, int renorm, int dtype, float* logits, int32_t* topk_ids,
+                    float* topk_weights, void* stream);
 
 /* Human-readable name of a status code; never NULL. */
 const char* moe_status_string(int status);

@@ -6,6 +6,7 @@ supplies device memory and the current stream; the binding checks dtypes,
 shapes, devices and contiguity (the C ABI sees raw pointers only) and raises
 MoeError with the library's status code on any failure.
 
+    ids, weights, logits = moe_gate(x, w_router, top_k)              # step 0
     tables = moe_dispatch(topk_ids, topk_weights, num_experts)      # step 1
     y = moe_routed_forward(x, w_gate, w_up, w_down, tables)         # steps 2-3
     y = moe_reduce_fused(expert_out, token_topk_to_pos, topk_weights)  # step 3 alone
@@ -19,7 +20,8 @@ from ._lib import (MOE_BF16, MOE_ERR_DTYPE, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_F16
                    MOE_FP8_E4M3,
                    MoeError, MoeTablesStruct, check, lib)
 
-__all__ = ["MoeError", "MoeTables", "default_block_m", "moe_dispatch", "moe_expert_gate_up",
+__all__ = ["MoeError", "MoeTables", "default_block_m", "moe_gate", "moe_dispatch",
+           "moe_expert_gate_up",
            "moe_expert_down", "moe_routed_forward", "moe_reduce_fused", "forward_workspace"]
 
 _DTYPE_CODE = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
@@ -103,6 +105,38 @@ class MoeTables:
         if name in _TABLE_FIELDS:
             return self.tensor(name)
         raise AttributeError(name)
+
+
+def moe_gate(x, w_router, top_k, renorm=True, bias=None, out=None):
+    """Step 0: router gate. x [T, H] (fp16 / bf16 / fp32), w_router [E, H]
+    float32, bias [E] float32 or None. Returns (topk_ids int32 [T, K],
+    topk_weights float32 [T, K], logits float32 [T, E]); `out` may pass
+    those three tensors to fill."""
+    _check_tensor(x, "x", None, 2)
+    _require(x.dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "x must be float16, bfloat16 or float32")
+    _check_tensor(w_router, "w_router", torch.float32, 2, x.device)
+    T, H = x.shape
+    E = w_router.shape[0]
+    _require(w_router.shape[1] == H, MOE_ERR_SHAPE, "w_router must be [E, %d]" % H)
+    if bias is not None:
+        _check_tensor(bias, "bias", torch.float32, 1, x.device)
+        _require(bias.shape[0] == E, MOE_ERR_SHAPE, "bias must be [%d]" % E)
+    K = int(top_k)
+    if out is None:
+        ids = torch.empty((T, K), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, K), dtype=torch.float32, device=x.device)
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    else:
+        ids, w, logits = out
+        _check_tensor(ids, "topk_ids", torch.int32, 2, x.device)
+        _check_tensor(w, "topk_weights", torch.float32, 2, x.device)
+        _check_tensor(logits, "logits", torch.float32, 2, x.device)
+        _require(tuple(ids.shape) == (T, K) and tuple(w.shape) == (T, K)
+                 and tuple(logits.shape) == (T, E), MOE_ERR_SHAPE, "output shapes do not match")
+    check(lib().moe_gate(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, K, int(bool(renorm)),
+                         _DTYPE_CODE[x.dtype], _ptr(logits), _ptr(ids), _ptr(w),
+                         _stream(x.device)))
+    return ids, w, logits
 
 
 def moe_dispatch(topk_ids, topk_weights, num_experts, block_m=None, tables=None):

@@ -73,6 +73,8 @@ def lib():
         L.moe_routed_forward.restype = i32
         L.moe_reduce_fused.argtypes = [vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_reduce_fused.restype = i32
+        L.moe_gate.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+        L.moe_gate.restype = i32
         L.moe_reduce_fused_scaled.argtypes = [vp, i64, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                               vp, vp]
         L.moe_reduce_fused_scaled.restype = i32

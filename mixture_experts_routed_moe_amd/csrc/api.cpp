@@ -187,6 +187,27 @@ moe_status moe_tables_bind(moe_tables* tables, void* buffer, size_t bytes, int T
   return ok();
 }
 
+moe_status moe_gate(const void* x, const float* w_router, const float* bias, int T, int H, int E,
+                    int K, int renorm, int dtype, float* logits, int32_t* topk_ids,
+                    float* topk_weights, void* stream) {
+  if (!x || !w_router || !logits || !topk_ids || !topk_weights) {
+    return fail(MOE_ERR_NULL, "x, w_router, logits, topk_ids and topk_weights must not be NULL");
+  }
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T must be >= 0 (got %d)", T);
+  if (H <= 0 || H % 64 != 0) {
+    return fail(MOE_ERR_SHAPE, "H must be a positive multiple of 64 (got %d)", H);
+  }
+  if (E < 1 || E > 1024) return fail(MOE_ERR_SHAPE, "E must be in [1, 1024] (got %d)", E);
+  if (K < 1 || K > 64 || K > E) {
+    return fail(MOE_ERR_SHAPE, "K must be in [1, min(E, 64)] (got K=%d, E=%d)", K, E);
+  }
+  if (!is_float(dtype)) return fail(MOE_ERR_DTYPE, "dtype must be MOE_F16, MOE_BF16 or MOE_F32");
+  if (T == 0) return ok();
+  return hip_status(moe::launch_gate(x, w_router, bias, T, H, E, K, renorm, dtype, logits,
+                                     topk_ids, topk_weights, static_cast<hipStream_t>(stream)),
+                    "moe_gate launch");
+}
+
 moe_status moe_dispatch(const int32_t* topk_ids, const float* topk_weights, moe_tables* tables,
                         void* stream) {
   if (!topk_ids) return fail(MOE_ERR_NULL, "topk_ids must not be NULL");

@@ -28,6 +28,10 @@ hipError_t launch_down(const GemmProblem& p, const moe_tables& t, hipStream_t st
 hipError_t launch_gate_up_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 
+hipError_t launch_gate(const void* x, const float* wr, const float* bias, int T, int H, int E,
+                       int K, int renorm, int dtype, float* logits, int32_t* ids, float* w,
+                       hipStream_t stream);
+
 hipError_t launch_reduce(const void* x, int64_t rows, const int32_t* pos, const float* w,
                          const float* x_sf, const float* sf, int T, int K, int H, int in_dtype,
                          int out_dtype, void* y, hipStream_t stream);

@@ -106,6 +106,22 @@ def test_calls_reject_bad_arguments_before_launching():
     assert L.moe_expert_down(fake, fake, ctypes.byref(s), 256, 128, 0, None, None) == 1
 
 
+def test_gate_rejects_bad_arguments_before_launching():
+    L = _lib.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    # moe_gate(x, w_router, bias, T, H, E, K, renorm, dtype, logits, ids, weights, stream)
+    assert L.moe_gate(None, fake, None, 4, 64, 8, 2, 1, 1, fake, fake, fake, None) == 1
+    assert L.moe_gate(fake, fake, None, 4, 64, 8, 2, 1, 1, None, fake, fake, None) == 1
+    assert L.moe_gate(fake, fake, None, 4, 96, 8, 2, 1, 1, fake, fake, fake, None) == 2
+    assert L.moe_gate(fake, fake, None, 4, 64, 2000, 2, 1, 1, fake, fake, fake, None) == 2
+    assert L.moe_gate(fake, fake, None, 4, 64, 8, 9, 1, 1, fake, fake, fake, None) == 2
+    assert L.moe_gate(fake, fake, None, 4, 64, 256, 65, 1, 1, fake, fake, fake, None) == 2
+    assert L.moe_gate(fake, fake, None, -1, 64, 8, 2, 1, 1, fake, fake, fake, None) == 2
+    assert L.moe_gate(fake, fake, None, 4, 64, 8, 2, 1, 3, fake, fake, fake, None) == 3
+    assert "dtype" in L.moe_last_error().decode()
+    assert L.moe_gate(fake, fake, None, 0, 64, 8, 2, 1, 1, fake, fake, fake, None) == 0
+
+
 def test_workspace_layout():
     L = _lib.lib()
     T, K, H, D = 512, 8, 7168, 2048
