@@ -45,6 +45,9 @@ def lib():
         L.oracle_reduce.argtypes = [i32, vp, i64, i32p, f32p, i32, i32, i32, f32p]
         L.oracle_reduce_scaled.argtypes = [i32, vp, i64, i32p, f32p, f32p, f32p, i32, i32, i32,
                                            f32p]
+        L.oracle_quantize_fp8_rows.argtypes = [i32, vp, i64, i32, vp, f32p]
+        L.oracle_moe_forward_w8.argtypes = [i32, vp, vp, vp, vp, f32p, f32p, f32p, i32p, f32p,
+                                            i32, i32, i32, i32, i32, i32p, i32, f32p, f32p, f32p]
         L.oracle_gate.argtypes = [i32, vp, f32p, f32p, i32, i32, i32, i32, i32, f32p, i32p, f32p]
         _lib = L
     return _lib
@@ -206,3 +209,38 @@ def gate(dt, x, wr, K, renorm, bias=None):
                            _ptr(logits), _ptr(ids), _ptr(w))
     assert rc == 0, "oracle_gate rejected its arguments"
     return dict(logits=logits, ids=ids, weights=w)
+
+
+def quantize_fp8_rows(dt, w):
+    """oracle_quantize_fp8_rows: per-row FP8 E4M3 codes and fp32 scales
+    (scale = amax / 448, 1 for a zero row). w: [..., cols] storage of dtype
+    dt. Returns (codes uint8 of w's shape, scales float32 of w's shape[:-1])."""
+    ws = _storage(np.asarray(w), dt)
+    cols = ws.shape[-1]
+    rows = ws.size // cols
+    q = np.empty(ws.shape, np.uint8)
+    s = np.empty(ws.shape[:-1], np.float32)
+    assert lib().oracle_quantize_fp8_rows(dt, _ptr(ws), rows, cols, _ptr(q), _ptr(s)) == 0
+    return q, s
+
+
+def moe_forward_w8(dt, x, wg8, wu8, wd8, sg, su, sd, ids, w, tokens=None, want_pairs=False):
+    """oracle_moe_forward_w8: the forward with FP8 expert weights (uint8 codes
+    [E, D, H] / [E, D, H] / [E, H, D]) and per-row fp32 scales ([E, D],
+    [E, D], [E, H]). Same outputs as moe_forward."""
+    xs = _storage(x, dt)
+    T, H = xs.shape
+    E, D, _ = wg8.shape
+    K = ids.shape[1]
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tokens is None else len(tok)
+    y = np.empty((n, H), np.float32)
+    hp = np.empty((n * K, D), np.float32) if want_pairs else None
+    ep = np.empty((n * K, H), np.float32) if want_pairs else None
+    args = [_c(a, np.uint8) for a in (wg8, wu8, wd8)] + [_c(a, np.float32) for a in (sg, su, sd)]
+    rc = lib().oracle_moe_forward_w8(dt, _ptr(xs), *[_ptr(a) for a in args], _ptr(ids), _ptr(w),
+                                     T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
+    assert rc == 0, "oracle_moe_forward_w8 rejected its arguments"
+    return (y, hp, ep) if want_pairs else y

@@ -166,29 +166,89 @@ bool reduce_dtype_ok(int dt) { return dtype_ok(dt) || dt == kFP8; }
 // exp2(-g*log2 e); the value is the same function, written here with expf.
 float silu(float g) { return g / (1.0f + std::exp(-g)); }
 
+// Expert weights as stored: dtype wdt (the activation dtype, or FP8 E4M3
+// with one fp32 scale per weight row, i.e. per output channel: sg / su [E*D]
+// for gate / up, sd [E*H] for down; NULL scales mean unscaled weights).
+struct ExpertWeights {
+  int wdt;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const float* sg;
+  const float* su;
+  const float* sd;
+};
+
 // One routed pair: token row x_t against expert e.
-//   g_j  = sum_h Wg[e,j,h] x[h]         u_j = sum_h Wu[e,j,h] x[h]
+//   g_j  = s_g[e,j] * sum_h Wg[e,j,h] x[h]   u_j = s_u[e,j] * sum_h Wu[e,j,h] x[h]
 //   h_j  = R(SiLU(g_j) * u_j)                    ([A] stage-1 epilogue)
-//   eo_c = R(sum_j Wd[e,c,j] h_j)                ([A] stage-2, unweighted)
-// W_gate/W_up are [E, D, H] and W_down is [E, H, D], row-major, so each dot
-// product walks a contiguous row ([A] "forward": stacked expert weights).
-void expert_pair(int dt, const float* xrow, const void* wg, const void* wu,
-                 const void* wd, int e, int H, int D, float* hbuf, float* eo) {
+//   eo_c = R(s_d[e,c] * sum_j Wd[e,c,j] h_j)     ([A] stage-2, unweighted)
+// (the scale factors apply to FP8 weights: each dot product runs over the
+// decoded FP8 values, then is multiplied by its row's scale once). W_gate /
+// W_up are [E, D, H] and W_down is [E, H, D], row-major, so each dot product
+// walks a contiguous row ([A] "forward": stacked expert weights).
+void expert_pair(int dt, const float* xrow, const ExpertWeights& W, int e, int H, int D,
+                 float* hbuf, float* eo) {
   for (int j = 0; j < D; ++j) {
     const int64_t row = (static_cast<int64_t>(e) * D + j) * H;
     float g = 0.0f, u = 0.0f;
     for (int k = 0; k < H; ++k) {
-      g = std::fma(load_elem(dt, wg, row + k), xrow[k], g);
-      u = std::fma(load_elem(dt, wu, row + k), xrow[k], u);
+      g = std::fma(load_elem(W.wdt, W.wg, row + k), xrow[k], g);
+      u = std::fma(load_elem(W.wdt, W.wu, row + k), xrow[k], u);
     }
+    if (W.sg) g = g * W.sg[static_cast<int64_t>(e) * D + j];
+    if (W.su) u = u * W.su[static_cast<int64_t>(e) * D + j];
     hbuf[j] = round_to(dt, silu(g) * u);
   }
   for (int c = 0; c < H; ++c) {
     const int64_t row = (static_cast<int64_t>(e) * H + c) * D;
     float o = 0.0f;
-    for (int j = 0; j < D; ++j) o = std::fma(load_elem(dt, wd, row + j), hbuf[j], o);
+    for (int j = 0; j < D; ++j) o = std::fma(load_elem(W.wdt, W.wd, row + j), hbuf[j], o);
+    if (W.sd) o = o * W.sd[static_cast<int64_t>(e) * H + c];
     eo[c] = round_to(dt, o);
   }
+}
+
+// The full forward over a token list (see oracle_moe_forward).
+int moe_forward(int dt, const void* x, const ExpertWeights& W, const int32_t* ids,
+                const float* w, int T, int H, int D, int E, int K, const int32_t* tokens,
+                int n_tokens, float* y, float* h_pairs, float* eo_pairs) {
+  if (!dtype_ok(dt) || T < 0 || H <= 0 || D <= 0 || E <= 0 || K <= 0) return -1;
+  if (!tokens && n_tokens != T) return -1;
+  for (int i = 0; i < n_tokens; ++i) {
+    const int t = tokens ? tokens[i] : i;
+    if (t < 0 || t >= T) return -1;
+    for (int k = 0; k < K; ++k) {
+      if (ids[static_cast<int64_t>(t) * K + k] >= E) return -1;
+    }
+  }
+#pragma omp parallel
+  {
+    std::vector<float> xrow(H), hbuf(D), eo(H), acc(H);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < n_tokens; ++i) {
+      const int t = tokens ? tokens[i] : i;
+      for (int c = 0; c < H; ++c) xrow[c] = load_elem(dt, x, static_cast<int64_t>(t) * H + c);
+      for (int c = 0; c < H; ++c) acc[c] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int64_t slot = static_cast<int64_t>(t) * K + k;
+        const int64_t out_slot = static_cast<int64_t>(i) * K + k;
+        const int e = ids[slot];
+        if (e < 0) {
+          if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = 0.0f;
+          if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = 0.0f;
+          continue;
+        }
+        expert_pair(dt, xrow.data(), W, e, H, D, hbuf.data(), eo.data());
+        const float wk = w[slot];
+        for (int c = 0; c < H; ++c) acc[c] = std::fma(wk, eo[c], acc[c]);
+        if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = hbuf[j];
+        if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = eo[c];
+      }
+      for (int c = 0; c < H; ++c) y[static_cast<int64_t>(i) * H + c] = acc[c];
+    }
+  }
+  return 0;
 }
 
 }  // namespace
@@ -314,7 +374,8 @@ int oracle_expert_pair(int dt, const void* x, const void* wg, const void* wu,
   if (!dtype_ok(dt) || H <= 0 || D <= 0) return -1;
   std::vector<float> xrow(H);
   for (int k = 0; k < H; ++k) xrow[k] = load_elem(dt, x, static_cast<int64_t>(token) * H + k);
-  expert_pair(dt, xrow.data(), wg, wu, wd, expert, H, D, h_out, eo_out);
+  const ExpertWeights W{dt, wg, wu, wd, nullptr, nullptr, nullptr};
+  expert_pair(dt, xrow.data(), W, expert, H, D, h_out, eo_out);
   return 0;
 }
 
@@ -334,42 +395,42 @@ int oracle_moe_forward(int dt, const void* x, const void* wg, const void* wu,
                        const void* wd, const int32_t* ids, const float* w, int T,
                        int H, int D, int E, int K, const int32_t* tokens,
                        int n_tokens, float* y, float* h_pairs, float* eo_pairs) {
-  if (!dtype_ok(dt) || T < 0 || H <= 0 || D <= 0 || E <= 0 || K <= 0) return -1;
-  if (!tokens && n_tokens != T) return -1;
-  for (int i = 0; i < n_tokens; ++i) {
-    const int t = tokens ? tokens[i] : i;
-    if (t < 0 || t >= T) return -1;
-    for (int k = 0; k < K; ++k) {
-      if (ids[static_cast<int64_t>(t) * K + k] >= E) return -1;
-    }
-  }
-#pragma omp parallel
-  {
-    std::vector<float> xrow(H), hbuf(D), eo(H), acc(H);
-#pragma omp for schedule(dynamic, 1)
-    for (int i = 0; i < n_tokens; ++i) {
-      const int t = tokens ? tokens[i] : i;
-      for (int c = 0; c < H; ++c) xrow[c] = load_elem(dt, x, static_cast<int64_t>(t) * H + c);
-      for (int c = 0; c < H; ++c) acc[c] = 0.0f;
-      for (int k = 0; k < K; ++k) {
-        const int64_t slot = static_cast<int64_t>(t) * K + k;
-        const int64_t out_slot = static_cast<int64_t>(i) * K + k;
-        const int e = ids[slot];
-        if (e < 0) {
-          if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = 0.0f;
-          if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = 0.0f;
-          continue;
-        }
-        expert_pair(dt, xrow.data(), wg, wu, wd, e, H, D, hbuf.data(), eo.data());
-        const float wk = w[slot];
-        for (int c = 0; c < H; ++c) acc[c] = std::fma(wk, eo[c], acc[c]);
-        if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = hbuf[j];
-        if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = eo[c];
-      }
-      for (int c = 0; c < H; ++c) y[static_cast<int64_t>(i) * H + c] = acc[c];
-    }
+  const ExpertWeights W{dt, wg, wu, wd, nullptr, nullptr, nullptr};
+  return moe_forward(dt, x, W, ids, w, T, H, D, E, K, tokens, n_tokens, y, h_pairs, eo_pairs);
+}
+
+// ------------------------------------------------ FP8 expert weights ------
+// Quantised expert weights (the pages leave the scheme open; taken here: OCP
+// FP8 E4M3 codes with one fp32 scale per weight row, i.e. per output
+// channel, activations in their own dtype). Per row r of `rows` rows of
+// `cols` values of dtype dt:
+//   amax = max_k |w[r, k]|,  s[r] = amax / 448 (1 for an all-zero row),
+//   q[r, k] = FP8(w[r, k] / s[r])   (fp32 division, round to nearest even,
+//                                     saturating at +-448).
+int oracle_quantize_fp8_rows(int dt, const void* w, int64_t rows, int cols, uint8_t* q,
+                             float* scales) {
+  if (!dtype_ok(dt) || rows < 0 || cols <= 0) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float amax = 0.0f;
+    for (int k = 0; k < cols; ++k) amax = std::fmax(amax, std::fabs(load_elem(dt, w, r * cols + k)));
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    scales[r] = s;
+    for (int k = 0; k < cols; ++k) q[r * cols + k] = float_to_fp8e4m3_bits(load_elem(dt, w, r * cols + k) / s);
   }
   return 0;
+}
+
+// The forward with FP8 expert weights and per-row scales (x, h, expert_out
+// and y as in oracle_moe_forward; see expert_pair for the scale placement).
+int oracle_moe_forward_w8(int dt, const void* x, const uint8_t* wg8, const uint8_t* wu8,
+                          const uint8_t* wd8, const float* sg, const float* su, const float* sd,
+                          const int32_t* ids, const float* w, int T, int H, int D, int E, int K,
+                          const int32_t* tokens, int n_tokens, float* y, float* h_pairs,
+                          float* eo_pairs) {
+  if (!sg || !su || !sd) return -1;
+  const ExpertWeights W{kFP8, wg8, wu8, wd8, sg, su, sd};
+  return moe_forward(dt, x, W, ids, w, T, H, D, E, K, tokens, n_tokens, y, h_pairs, eo_pairs);
 }
 
 // -------------------------------------------------------- weighted reduce --
