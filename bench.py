@@ -33,7 +33,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pmc_grouped_gemm_gate_up_deepseek_decode.md")
 GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", f)
-                for f in ("grouped_gemm.hip", "common.hpp")]
+                for f in ("grouped_gemm.hpp", "grouped_gemm.hip", "common.hpp")]
 
 
 def parse_args():
@@ -77,29 +77,35 @@ def counter_traffic():
     return float(val.group(1))
 
 
-def workload_numbers(d, tables_sizes):
+def workload_numbers(d, tables_sizes, fp8_weights=False):
     """Algorithmic FLOPs and bytes of one step, per kernel (units in the
-    design notes): weights of the experts that receive rows once, x read
-    once, h / expert_out written and read once, y written once."""
+    design notes): weights of the experts that receive rows once (FP8
+    weights: 1 byte each plus a 4-byte scale per row), x read once, h /
+    expert_out written and read once, y written once."""
     T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
     b = d["x"].element_size()
+    wb = 1 if fp8_weights else b
+    sc = 4 if fp8_weights else 0          # scale bytes per weight row
     n_valid = int(tables_sizes.sum())
     e_active = int((tables_sizes > 0).sum())
     P = T * K
-    gate_up_bytes = e_active * 2 * D * H * b + T * H * b + n_valid * D * b
-    down_bytes = e_active * H * D * b + n_valid * D * b + n_valid * H * b
+    gate_up_bytes = e_active * 2 * D * (H * wb + sc) + T * H * b + n_valid * D * b
+    down_bytes = e_active * H * (D * wb + sc) + n_valid * D * b + n_valid * H * b
     reduce_bytes = n_valid * H * b + T * H * b + P * 8
     dispatch_bytes = P * 8 + n_valid * 12 + P * 8 + 12 * E
     flops_gate_up = 4 * n_valid * H * D
     flops_down = 2 * n_valid * H * D
-    b_min = e_active * 3 * H * D * b + 2 * T * H * b + P * 8
+    b_min = e_active * 3 * H * D * wb + e_active * (2 * D + H) * sc + 2 * T * H * b + P * 8
     return dict(n_valid=n_valid, e_active=e_active, gate_up_bytes=gate_up_bytes,
                 down_bytes=down_bytes, reduce_bytes=reduce_bytes, dispatch_bytes=dispatch_bytes,
                 flops_gate_up=flops_gate_up, flops_down=flops_down,
                 flops=flops_gate_up + flops_down, b_min=b_min)
 
 
-def time_workload(cfg, steps, warmup, block_m, dev):
+def time_workload(cfg, steps, warmup, block_m, dev, fp8_weights=False):
+    """One workload's step timed kernel by kernel. fp8_weights: the expert
+    weights are quantized once (moe_quantize_fp8_rows, timed on its own, not
+    part of the step) and the step runs the FP8-weight GEMMs."""
     import torch
 
     import mixture_experts_routed_moe_amd as mr
@@ -109,6 +115,15 @@ def time_workload(cfg, steps, warmup, block_m, dev):
     d = S.make_moe_inputs(cfg, device=dev)
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
+    quant_ms = None
+    if fp8_weights:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        q = [mr.quantize_fp8_rows(d[n]) for n in ("w_gate", "w_up", "w_down")]
+        ev[1].record()
+        torch.cuda.synchronize()
+        quant_ms = ev[0].elapsed_time(ev[1])
+        d["w_gate"], d["w_up"], d["w_down"] = q
     T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
     block_m = block_m or mr.default_block_m(T, K, E)
     ids, w = d["topk_ids"], d["topk_weights"]
@@ -123,9 +138,14 @@ def time_workload(cfg, steps, warmup, block_m, dev):
         ev[0].record()
         mr.moe_dispatch(ids, w, E, block_m=block_m, tables=tables)
         ev[1].record()
-        mr.moe_expert_gate_up(x, wg, wu, tables, h=h)
-        ev[2].record()
-        mr.moe_expert_down(h, wd, tables, expert_out=eo)
+        if fp8_weights:
+            mr.moe_expert_gate_up_w8(x, wg, wu, tables, h=h)
+            ev[2].record()
+            mr.moe_expert_down_w8(h, wd, tables, expert_out=eo)
+        else:
+            mr.moe_expert_gate_up(x, wg, wu, tables, h=h)
+            ev[2].record()
+            mr.moe_expert_down(h, wd, tables, expert_out=eo)
         ev[3].record()
         mr.moe_reduce_fused(eo, pos, wt, y=y)
         ev[4].record()
@@ -146,9 +166,9 @@ def time_workload(cfg, steps, warmup, block_m, dev):
            for j, n in enumerate(names)}
     span = sum(ev[0].elapsed_time(ev[4]) for ev in events) / steps
     sizes = tables.group_sizes.cpu()
-    nums = workload_numbers(d, sizes)
+    nums = workload_numbers(d, sizes, fp8_weights)
     return dict(d=d, tables=tables, block_m=block_m, wall_ms=wall_ms, event_ms=span,
-                kernel_ms=per, nums=nums, gen_s=t_gen)
+                kernel_ms=per, nums=nums, gen_s=t_gen, quant_ms=quant_ms)
 
 
 def summarize(r):
@@ -434,6 +454,17 @@ def main():
         torch.cuda.empty_cache()
         extras["gate"] = time_gate(args.steps, args.warmup, dev)
         torch.cuda.empty_cache()
+        fp8 = {}
+        for ci in (2, 3):
+            r8 = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev, fp8_weights=True)
+            r8.pop("d")
+            r8.pop("tables")
+            torch.cuda.empty_cache()
+            s8 = summarize(r8)
+            s8["quantize_ms"] = round(r8["quant_ms"], 3)
+            s8["workload"] = S.CONFIGS[ci]["name"] + " with FP8 E4M3 expert weights (per-row scales)"
+            fp8["T%d" % S.CONFIGS[ci]["T"]] = s8
+        extras["fp8_weights"] = fp8
         print("# %s" % json.dumps(extras), file=sys.stderr, flush=True)
 
     gu = main_s["kernels"]["gate_up"]
@@ -465,6 +496,7 @@ def main():
         "reduce_skewed": extras.get("reduce_skewed"),
         "mfma_probe": extras.get("mfma_probe"),
         "gate": extras.get("gate"),
+        "fp8_weights": extras.get("fp8_weights"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -216,6 +216,42 @@ moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_u
                               int dtype, void* workspace, size_t workspace_bytes, void* y,
                               void* stream);
 
+/* Quantised expert weights (FP8 E4M3 with one fp32 scale per weight row,
+ * i.e. per output channel; activations, h, expert_out and y stay in the
+ * 16-bit dtype). The pages leave the quantisation scheme open; this one
+ * halves the weight bytes the decode layer streams.
+ *
+ * moe_quantize_fp8_rows: for each of `rows` rows of `cols` values of dtype
+ * (MOE_F16, MOE_BF16, MOE_F32) in w, writes
+ *   scales[r] = max_k |w[r,k]| / 448 (1 for an all-zero row) and
+ *   q[r, k]   = E4M3(w[r, k] / scales[r])  (fp32 division, round to nearest
+ *               even, saturating at +-448).
+ * Stacked weights [E, N, Kd] are E*N rows of Kd. A one-time conversion.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP. */
+moe_status moe_quantize_fp8_rows(const void* w, int64_t rows, int cols, int dtype, uint8_t* q,
+                                 float* scales, void* stream);
+
+/* moe_expert_gate_up / moe_expert_down with FP8 weights: w_gate, w_up
+ * [E, D, H] and w_down [E, H, D] hold E4M3 codes; s_gate, s_up [E, D] and
+ * s_down [E, H] the fp32 row scales. Each dot product runs over the decoded
+ * codes (exact in the 16-bit dtype), then is multiplied by its row's scale:
+ *   g = s_gate[e,j] * (x . Wg8[e,j]),  u = s_up[e,j] * (x . Wu8[e,j]),
+ *   h = R(SiLU(g) * u),  expert_out[i,c] = R(s_down[e,c] * (h . Wd8[e,c])).
+ * dtype: MOE_F16 or MOE_BF16. Other requirements and errors as the 16-bit
+ * calls. moe_routed_forward_w8 runs both and moe_reduce_fused (workspace as
+ * moe_routed_forward). */
+moe_status moe_expert_gate_up_w8(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                 const float* s_gate, const float* s_up, const moe_tables* tables,
+                                 int H, int D, int dtype, void* h, void* stream);
+moe_status moe_expert_down_w8(const void* h, const uint8_t* w_down, const float* s_down,
+                              const moe_tables* tables, int H, int D, int dtype, void* expert_out,
+                              void* stream);
+moe_status moe_routed_forward_w8(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                 const uint8_t* w_down, const float* s_gate, const float* s_up,
+                                 const float* s_down, const moe_tables* tables, int H, int D,
+                                 int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                 void* stream);
+
 /* Step 3: top-k weighted reduce back to token order ([C] sections 1-2):
  *   y[t, :] = R_out( sum over k = 0..K-1 ascending with pos[t,k] >= 0 of
  *                    w[t,k] * expert_out[pos[t,k], :] )

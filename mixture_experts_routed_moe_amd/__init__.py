@@ -20,8 +20,9 @@ from ._lib import (MOE_BF16, MOE_ERR_DTYPE, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_F16
                    MOE_FP8_E4M3,
                    MoeError, MoeTablesStruct, check, lib)
 
-__all__ = ["MoeError", "MoeTables", "default_block_m", "moe_gate", "moe_dispatch",
-           "moe_expert_gate_up",
+__all__ = ["MoeError", "MoeTables", "FP8Weights", "default_block_m", "moe_gate", "moe_dispatch",
+           "quantize_fp8_rows", "moe_expert_gate_up_w8", "moe_expert_down_w8",
+           "moe_routed_forward_w8", "moe_expert_gate_up",
            "moe_expert_down", "moe_routed_forward", "moe_reduce_fused", "forward_workspace"]
 
 _DTYPE_CODE = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
@@ -242,6 +243,100 @@ def moe_routed_forward(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
     check(lib().moe_routed_forward(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), tables.ref,
                                    H, D, _DTYPE_CODE[x.dtype], _ptr(workspace),
                                    workspace.numel(), _ptr(y), _stream(x.device)))
+    return y
+
+
+class FP8Weights:
+    """Stacked expert weights in FP8 E4M3: `codes` uint8 [E, N, Kd] and one
+    fp32 scale per row, `scales` [E, N] (value = scale * decoded code)."""
+
+    def __init__(self, codes, scales):
+        _check_tensor(codes, "codes", torch.uint8, 3)
+        _check_tensor(scales, "scales", torch.float32, 2, codes.device)
+        _require(tuple(scales.shape) == tuple(codes.shape[:2]), MOE_ERR_SHAPE,
+                 "scales must be [E, N] = %s" % (tuple(codes.shape[:2]),))
+        self.codes = codes
+        self.scales = scales
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+    def dim(self):
+        return 3
+
+
+def quantize_fp8_rows(w):
+    """moe_quantize_fp8_rows on stacked weights w [E, N, Kd] (fp16 / bf16 /
+    fp32): per-row scale amax / 448 and E4M3 codes. Returns FP8Weights."""
+    _check_tensor(w, "w", None, 3)
+    _require(w.dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "w must be float16, bfloat16 or float32")
+    E, N, Kd = w.shape
+    codes = torch.empty((E, N, Kd), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, N), dtype=torch.float32, device=w.device)
+    check(lib().moe_quantize_fp8_rows(_ptr(w), E * N, Kd, _DTYPE_CODE[w.dtype], _ptr(codes),
+                                      _ptr(scales), _stream(w.device)))
+    return FP8Weights(codes, scales)
+
+
+def _check_w8(w, name, device):
+    _require(isinstance(w, FP8Weights), MOE_ERR_DTYPE, "%s must be FP8Weights" % name)
+    _require(w.codes.device == device, MOE_ERR_SHAPE, "%s is on another device" % name)
+
+
+def moe_expert_gate_up_w8(x, w_gate, w_up, tables, h=None):
+    """Step 2a with FP8 weights (FP8Weights [E, D, H]); x and h 16-bit."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    _require(x.dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "FP8 weights take float16 or bfloat16 activations")
+    for n, w in (("w_gate", w_gate), ("w_up", w_up)):
+        _check_w8(w, n, tables.device)
+    H, D = _expert_shapes(x, w_gate, w_up, None, tables, True)
+    if h is None:
+        h = torch.empty(tables.T * tables.K, D, dtype=x.dtype, device=x.device)
+    _check_tensor(h, "h", x.dtype, 2, tables.device)
+    check(lib().moe_expert_gate_up_w8(_ptr(x), _ptr(w_gate.codes), _ptr(w_up.codes),
+                                      _ptr(w_gate.scales), _ptr(w_up.scales), tables.ref, H, D,
+                                      _DTYPE_CODE[x.dtype], _ptr(h), _stream(x.device)))
+    return h
+
+
+def moe_expert_down_w8(h, w_down, tables, expert_out=None):
+    """Step 2b with FP8 weights (FP8Weights [E, H, D]); h and expert_out 16-bit."""
+    _check_tensor(h, "h", None, 2, tables.device)
+    _require(h.dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "FP8 weights take float16 or bfloat16 activations")
+    _check_w8(w_down, "w_down", tables.device)
+    H, D = _expert_shapes(h, w_down, None, None, tables, False)
+    if expert_out is None:
+        expert_out = torch.empty(tables.T * tables.K, H, dtype=h.dtype, device=h.device)
+    _check_tensor(expert_out, "expert_out", h.dtype, 2, tables.device)
+    check(lib().moe_expert_down_w8(_ptr(h), _ptr(w_down.codes), _ptr(w_down.scales), tables.ref,
+                                   H, D, _DTYPE_CODE[h.dtype], _ptr(expert_out),
+                                   _stream(h.device)))
+    return expert_out
+
+
+def moe_routed_forward_w8(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
+    """Steps 2-3 with FP8 weights: y [T, H] of x.dtype."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    _require(x.dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "FP8 weights take float16 or bfloat16 activations")
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_w8(w, n, tables.device)
+    H, D = _expert_shapes(x, w_gate, w_up, w_down, tables, True)
+    if workspace is None:
+        workspace = forward_workspace(tables, H, D, x.dtype)[0]
+    _check_tensor(workspace, "workspace", torch.uint8, 1, tables.device)
+    if y is None:
+        y = torch.empty(tables.T, H, dtype=x.dtype, device=x.device)
+    _check_tensor(y, "y", x.dtype, 2, tables.device)
+    _require(tuple(y.shape) == (tables.T, H), MOE_ERR_SHAPE, "y must be [T, H]")
+    check(lib().moe_routed_forward_w8(_ptr(x), _ptr(w_gate.codes), _ptr(w_up.codes),
+                                      _ptr(w_down.codes), _ptr(w_gate.scales),
+                                      _ptr(w_up.scales), _ptr(w_down.scales), tables.ref, H, D,
+                                      _DTYPE_CODE[x.dtype], _ptr(workspace), workspace.numel(),
+                                      _ptr(y), _stream(x.device)))
     return y
 
 

@@ -73,6 +73,15 @@ def lib():
         L.moe_routed_forward.restype = i32
         L.moe_reduce_fused.argtypes = [vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.moe_reduce_fused.restype = i32
+        L.moe_quantize_fp8_rows.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.moe_quantize_fp8_rows.restype = i32
+        L.moe_expert_gate_up_w8.argtypes = [vp, vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_gate_up_w8.restype = i32
+        L.moe_expert_down_w8.argtypes = [vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_down_w8.restype = i32
+        L.moe_routed_forward_w8.argtypes = [vp, vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp, sz,
+                                            vp, vp]
+        L.moe_routed_forward_w8.restype = i32
         L.moe_gate.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         L.moe_gate.restype = i32
         L.moe_reduce_fused_scaled.argtypes = [vp, i64, vp, vp, vp, vp, i32, i32, i32, i32, i32,

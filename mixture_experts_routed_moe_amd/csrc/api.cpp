@@ -283,6 +283,81 @@ moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_u
   return hip_status(err, "moe_routed_forward reduce launch");
 }
 
+moe_status moe_quantize_fp8_rows(const void* w, int64_t rows, int cols, int dtype, uint8_t* q,
+                                 float* scales, void* stream) {
+  if (!w || !q || !scales) return fail(MOE_ERR_NULL, "w, q and scales must not be NULL");
+  if (rows < 0 || cols <= 0) return fail(MOE_ERR_SHAPE, "rows must be >= 0 and cols > 0");
+  if (rows > (int64_t{1} << 33)) return fail(MOE_ERR_SHAPE, "too many rows for one launch");
+  if (!is_float(dtype)) return fail(MOE_ERR_DTYPE, "dtype must be MOE_F16, MOE_BF16 or MOE_F32");
+  if (rows == 0) return ok();
+  return hip_status(moe::launch_quantize_fp8_rows(w, rows, cols, dtype, q, scales,
+                                                  static_cast<hipStream_t>(stream)),
+                    "moe_quantize_fp8_rows launch");
+}
+
+moe_status moe_expert_gate_up_w8(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                 const float* s_gate, const float* s_up, const moe_tables* tables,
+                                 int H, int D, int dtype, void* h, void* stream) {
+  if (!x || !w_gate || !w_up || !s_gate || !s_up || !h) {
+    return fail(MOE_ERR_NULL, "x, w_gate, w_up, s_gate, s_up and h must not be NULL");
+  }
+  moe_status s = check_expert_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (!is_16bit(dtype)) return fail(MOE_ERR_DTYPE, "FP8 weights take MOE_F16 or MOE_BF16 activations");
+  moe::GemmProblem p{x, w_gate, w_up, h, D, H, dtype, s_gate, s_up};
+  return hip_status(moe::launch_gate_up_w8(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_gate_up_w8 launch");
+}
+
+moe_status moe_expert_down_w8(const void* h, const uint8_t* w_down, const float* s_down,
+                              const moe_tables* tables, int H, int D, int dtype, void* expert_out,
+                              void* stream) {
+  if (!h || !w_down || !s_down || !expert_out) {
+    return fail(MOE_ERR_NULL, "h, w_down, s_down and expert_out must not be NULL");
+  }
+  moe_status s = check_expert_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (!is_16bit(dtype)) return fail(MOE_ERR_DTYPE, "FP8 weights take MOE_F16 or MOE_BF16 activations");
+  moe::GemmProblem p{h, w_down, nullptr, expert_out, H, D, dtype, s_down, nullptr};
+  return hip_status(moe::launch_down_w8(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_down_w8 launch");
+}
+
+moe_status moe_routed_forward_w8(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                 const uint8_t* w_down, const float* s_gate, const float* s_up,
+                                 const float* s_down, const moe_tables* tables, int H, int D,
+                                 int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                 void* stream) {
+  if (!x || !w_gate || !w_up || !w_down || !s_gate || !s_up || !s_down || !workspace || !y) {
+    return fail(MOE_ERR_NULL,
+                "x, the weights, their scales, workspace and y must not be NULL");
+  }
+  moe_status s = check_expert_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (!is_16bit(dtype)) return fail(MOE_ERR_DTYPE, "FP8 weights take MOE_F16 or MOE_BF16 activations");
+  const size_t need = moe_forward_workspace_bytes(tables->T, tables->K, H, D, dtype);
+  if (workspace_bytes < need) {
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) {
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  char* ws = static_cast<char*>(workspace);
+  void* hbuf = ws;
+  void* eo = ws + moe_forward_workspace_expert_out_offset(tables->T, tables->K, H, D, dtype);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe::GemmProblem up{x, w_gate, w_up, hbuf, D, H, dtype, s_gate, s_up};
+  hipError_t err = moe::launch_gate_up_w8(up, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w8 gate/up launch");
+  moe::GemmProblem down{hbuf, w_down, nullptr, eo, H, D, dtype, s_down, nullptr};
+  err = moe::launch_down_w8(down, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w8 down launch");
+  const int64_t P = static_cast<int64_t>(tables->T) * tables->K;
+  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
+                           nullptr, tables->T, tables->K, H, dtype, dtype, y, st);
+  return hip_status(err, "moe_routed_forward_w8 reduce launch");
+}
+
 moe_status moe_reduce_fused_scaled(const void* expert_out, int64_t rows,
                                    const int32_t* token_topk_to_pos, const float* topk_weights,
                                    const float* x_sf, const float* sf, int T, int K, int H,

@@ -1,0 +1,695 @@
+// Grouped expert GEMMs of the routed MoE forward on gfx950 (bf16/fp16 MFMA):
+// the kernel templates, shared by grouped_gemm.hip (weights in the
+// activation dtype) and grouped_gemm_w8.hip (FP8 E4M3 weights).
+//
+// What is computed ("tilelang baseline" MoE walkthrough, devpress.csdn.net,
+// sections "stage-1 gate+up" and "stage-2 down"; TileLang tutorial ch.18
+// skeletons.py, moe_routed_kernel):
+//   gate/up: h[i, j]  = R( SiLU(x_t . Wg[e, j]) * (x_t . Wu[e, j]) ),
+//            t = sorted_token[i], e = the expert of sorted row i;
+//   down:    eo[i, c] = R( h[i] . Wd[e, c] )   (no routing weight here).
+// Each workgroup takes one row block of the dispatch tables and one tile of
+// output columns, finds its expert and rows from the tables exactly as the
+// pages' kernels do (m_start = bx*BM - padded[e] + offset[e], rows =
+// min(BM, size[e] - (bx*BM - padded[e]))), and exits at once when the block
+// holds no rows, where the pages' kernels load and discard.
+//
+// Tile design for CDNA4 (not a translation of the pages' 128x128x128 tiles):
+//   * 256 threads = 4 waves. Each wave owns 32 output columns of BOTH gate
+//     and up (gate/up), or 64 columns (down), and ALL rows of the block, so
+//     a weight element is fetched from HBM once per block and feeds every
+//     row's MFMA: weights never go through LDS and are not shared between
+//     waves. The weight stream goes straight from global memory into the
+//     B-operand registers of v_mfma_f32_32x32x16_{bf16,f16}.
+//   * The reduction is walked in chunks of 64 elements. Inside a chunk the
+//     MFMA k-order is permuted so that lane half h (lane / 32) owns the 32
+//     consecutive elements [32h, 32h + 32): every lane then loads 64
+//     contiguous bytes of one weight row, two lanes cover a 128-byte row
+//     segment, and A uses the same permutation (a sum over k does not care
+//     about its order as long as A and B agree).
+//   * The A rows of the block (token rows of x gathered through
+//     sorted_token for gate/up; contiguous h rows for down) are shared by the
+//     4 waves through a double-buffered LDS tile; every A fragment read from
+//     LDS feeds two MFMAs. One barrier per chunk.
+//   * Software pipeline: the loads of chunk c+S-1 are issued while chunk c
+//     is multiplied (S-1 chunks of weights in flight).
+//   * Row groups of 32 rows with no valid row skip their MFMAs, so a block
+//     with 16 rows of a 32/64-row tile costs one row group of MFMA work.
+//   * Only blocks that hold rows are scheduled (the dispatch's active-block
+//     list), and they are mapped XCD-aware: workgroup L runs on XCD L % 8, so
+//     the natural tile order (active block major, column tile minor) is dealt
+//     out in equal contiguous ranges per XCD. The column tiles of one row
+//     block then share the A rows in that XCD's L2.
+// Two kernels share this design:
+//   * grouped_gemm_kernel, blocks of <= 64 rows (decode-sized groups): up to
+//     2 row groups of accumulators, A staged through registers and a padded
+//     LDS tile; small enough for two workgroups per CU.
+//   * grouped_gemm_wide_kernel, blocks of 128 or 256 rows (prefill-sized
+//     groups): up to 6 row groups (192 rows) in one pass over the weights,
+//     one workgroup per CU using all 512 registers of each wave, A rows in
+//     a swizzled LDS layout. A whole prefill-sized expert group then streams
+//     its weights once, where smaller blocks would stream them once per
+//     block.
+
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunkK = 64;
+constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
+// Pipeline depths (chunks in flight), measured on MI355X: blocks of <= 32
+// rows stream gate/up best at depth 4 and down (half the bytes per column
+// tile, more workgroups) at depth 2; 64-row blocks at depth 4. The wide
+// kernel runs at depth 4 (registers: 6 row groups of accumulators, the
+// weight ring and the A ring fill the 512 registers of one wave per SIMD).
+#ifndef MOE_W8_RG1_STAGES
+#define MOE_W8_RG1_STAGES 6
+#endif
+#ifndef MOE_RG1_DOWN_STAGES
+#define MOE_RG1_DOWN_STAGES 2
+#endif
+constexpr int kStagesRG1 = 4;
+constexpr int kStagesRG1Down = MOE_RG1_DOWN_STAGES;
+constexpr int kStagesRG2 = 4;
+constexpr int kStagesWide = 4;
+
+struct GemmArgs {
+  const uint16_t* a;
+  const void* b0;      // weights: 16-bit values, or FP8 E4M3 codes (W8)
+  const void* b1;
+  const float* s0;     // W8: fp32 scale per row of b0 / b1 (one per output channel)
+  const float* s1;
+  uint16_t* c;
+  const int32_t* sorted_token;
+  const int32_t* group_sizes;
+  const int32_t* group_offsets;
+  const int32_t* group_padded_offsets;
+  const int32_t* block_expert;
+  const int32_t* active_blocks;
+  const int32_t* active_count;
+  int n, kd, block_m, n_tiles;
+};
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// One chunk of a wave's weights: for each of its two weight rows, the lane's
+// 32 reduction elements as loaded -- 16-bit values (4 x 16 bytes) or FP8 E4M3
+// codes (W8: 2 x 16 bytes) -- and their MFMA B operand for k-slice t (8
+// 16-bit values, elements 8t..8t+7 of the lane's 32). FP8 codes are decoded
+// to the activation dtype, exactly (every E4M3 value is a bf16 and an fp16
+// value), two per v_cvt_scalef32_pk instruction with scale 1.
+template <int DT, bool W8>
+struct BChunk {
+  static constexpr int kVec = W8 ? 2 : 4;
+  u32x4 v[2][kVec];
+
+  // p: the lane's two row pointers (byte addresses); off: reduction offset.
+  __device__ __forceinline__ void load(const uint8_t* const* p, int64_t off) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        v[j][i] = *reinterpret_cast<const u32x4*>(p[j] + off * (W8 ? 1 : 2) + i * 16);
+      }
+    }
+  }
+
+  __device__ __forceinline__ u32x4 operand(int j, int t) const {
+    if constexpr (!W8) {
+      return v[j][t];
+    } else {
+      const u32x4 raw = v[j][t >> 1];
+      const uint32_t d0 = (t & 1) ? raw.z : raw.x;
+      const uint32_t d1 = (t & 1) ? raw.w : raw.y;
+      return u32x4{dec2(d0, false), dec2(d0, true), dec2(d1, false), dec2(d1, true)};
+    }
+  }
+
+ private:
+  // Two FP8 codes (bytes 0-1, or 2-3 with hi) -> two 16-bit values.
+  static __device__ __forceinline__ uint32_t dec2(uint32_t d, bool hi) {
+    if constexpr (DT == kBF16) {
+      return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true))
+                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false));
+    } else {
+      return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true))
+                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false));
+    }
+  }
+};
+
+template <int N>
+using int_c = std::integral_constant<int, N>;
+
+// Calls f(int_c<0>{}), ..., f(int_c<N-1>{}): a loop whose index is a
+// compile-time constant in every iteration (register-ring slots stay static).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(int_c<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The two weight rows a lane streams and their scales: gate/up -- row col0
+// + lane%32 of W_gate and of W_up (col0 = 128*nt + 32*wave); down -- rows
+// col0 + lane%32 and col0 + 32 + lane%32 of W_down (col0 = 256*nt +
+// 64*wave). The lane starts at reduction element 32*(lane/32) of each row.
+template <bool GATEUP, bool W8>
+__device__ __forceinline__ void weight_rows(const GemmArgs& g, int e, int nt, int wave, int lr,
+                                            int lh, int& col0, const uint8_t** bptr,
+                                            float* scale) {
+  const int64_t kd = g.kd;
+  const int64_t eb = W8 ? 1 : 2;   // bytes per weight element
+  const int64_t expert_row0 = static_cast<int64_t>(e) * g.n;
+  int64_t row[2];
+  if constexpr (GATEUP) {
+    col0 = nt * 128 + wave * 32;
+    row[0] = expert_row0 + col0 + lr;
+    row[1] = row[0];
+  } else {
+    col0 = nt * 256 + wave * 64;
+    row[0] = expert_row0 + col0 + lr;
+    row[1] = row[0] + 32;
+  }
+  const uint8_t* b0 = static_cast<const uint8_t*>(g.b0);
+  const uint8_t* b1 = static_cast<const uint8_t*>(GATEUP ? g.b1 : g.b0);
+  bptr[0] = b0 + (row[0] * kd + lh * 32) * eb;
+  bptr[1] = b1 + (row[1] * kd + lh * 32) * eb;
+  if constexpr (W8) {
+    scale[0] = g.s0[row[0]];
+    scale[1] = (GATEUP ? g.s1 : g.s0)[row[1]];
+  } else {
+    scale[0] = scale[1] = 1.0f;
+  }
+}
+
+// One pass over the reduction for NA active row groups (NA*32 rows) of the
+// block, with a software pipeline of depth S: the A share and the B
+// fragments of chunk c+S-1 are loaded while chunk c is multiplied. The loads
+// of a chunk are issued A first, then B; since vector loads complete in issue
+// order, waiting for the A share of chunk c+1 (to stage it in LDS) never
+// waits for B fragments of later chunks, so S-1 chunks of weights stay in
+// flight across the per-chunk barrier. The loop body is straight-line (no
+// branch touches the accumulators, so they stay in place); the last chunks
+// run as a guarded tail without prefetches past the end.
+template <int DT, int NA, int RG, bool GATEUP, int S, bool W8>
+__device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[32 * RG][kLdsRow],
+                                          const uint16_t* const* asrc,
+                                          const uint8_t* const* bptr, const float* scale,
+                                          int nchunks, int rot, int a_row, int a_seg, int lr,
+                                          int lh, int64_t out_row0, int rows_pass, int col0) {
+  f32x16 acc[NA][2];
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+    acc[q][0] = f32x16{};
+    acc[q][1] = f32x16{};
+  }
+  u32x4 aring[S][NA];
+  BChunk<DT, W8> bring[S];
+
+  auto load_chunk = [&](int c, int slot) {
+    int cc = c + rot;
+    if (cc >= nchunks) cc -= nchunks;
+    const int64_t off = static_cast<int64_t>(cc) * kChunkK;
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      if (a_row + 32 * q < rows_pass) aring[slot][q] = load16(asrc[q] + off);
+    }
+    bring[slot].load(bptr, off);
+  };
+  auto stage_a = [&](int slot, int buf) {
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      if (a_row + 32 * q < rows_pass) *reinterpret_cast<u32x4*>(&lds_a[buf][a_row + 32 * q][a_seg * 8]) = aring[slot][q];
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) load_chunk(st, st);
+  stage_a(0, 0);
+  __syncthreads();
+
+  // One chunk: prefetch chunk c+S-1 (only while it exists: nothing past the
+  // end is ever loaded), multiply chunk c, stage chunk c+1's A share,
+  // barrier. U = c % S (the register slot).
+  static_assert(S % 2 == 0, "the LDS buffer of chunk c is c % 2 == slot % 2");
+  auto step = [&](int c, auto U, bool prefetch, bool stage) {
+    constexpr int u = decltype(U)::value;
+    if (prefetch) load_chunk(c + S - 1, (u + S - 1) % S);
+    constexpr int buf = u & 1;   // S is even, so c & 1 == u & 1
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(&lds_a[buf][q * 32 + lr][lh * 32 + t * 8]);
+        acc[q][0] = mfma32x32x16<DT>(a, bring[u].operand(0, t), acc[q][0]);
+        acc[q][1] = mfma32x32x16<DT>(a, bring[u].operand(1, t), acc[q][1]);
+      }
+    }
+    if (stage) stage_a((u + 1) % S, buf ^ 1);
+    __syncthreads();
+  };
+  // Full groups of S steps while every step's prefetch exists, then the last
+  // S..2S-1 chunks as a guarded tail (S need not divide the chunk count).
+  int c0 = 0;
+  for (; c0 + 2 * S - 1 <= nchunks - 1; c0 += S) {
+    static_for<S>([&](auto U) { step(c0 + U, U, true, true); });
+  }
+  const int rem = nchunks - c0;
+  static_for<2 * S>([&](auto U) {
+    constexpr int u = decltype(U)::value;
+    if (u < rem) step(c0 + u, int_c<u % S>{}, u + S - 1 < rem, u + 1 < rem);
+  });
+
+  // Epilogue. MFMA 32x32 accumulator layout: lane l holds column l % 32 and,
+  // in register i, row 8*(i/4) + 4*(l/32) + i%4 of the 32x32 tile.
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = q * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+      if (row < rows_pass) {
+        uint16_t* out = g.c + (out_row0 + row) * g.n + col0 + lr;
+        float v0 = acc[q][0][i], v1 = acc[q][1][i];
+        if constexpr (W8) {   // the rows' scales, once per dot product
+          v0 *= scale[0];
+          v1 *= scale[1];
+        }
+        if constexpr (GATEUP) {
+          out[0] = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
+        } else {
+          out[0] = static_cast<uint16_t>(from_float<DT>(v0));
+          out[32] = static_cast<uint16_t>(from_float<DT>(v1));
+        }
+      }
+    }
+  }
+}
+
+// RG = row groups of 32 rows per pass (a pass covers 32*RG rows of the
+// block); GATEUP selects the gate/up kernel (two weight matrices, gathered A,
+// SiLU(gate)*up epilogue) or the down kernel (one matrix, 64 columns per
+// wave, contiguous A); S = software-pipeline depth in chunks.
+template <int DT, int RG, bool GATEUP, int S, bool W8>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][32 * RG][kLdsRow];
+
+  // Only blocks that hold rows are scheduled: the grid is sized for every
+  // block, and workgroups past the active work exit at once.
+  const int total = g.active_count[0] * g.n_tiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
+  const int ab = natural / g.n_tiles;
+  const int nt = natural - ab * g.n_tiles;
+  const int bx = g.active_blocks[ab];
+
+  const int e = g.block_expert[bx];
+  const int row_in_group = bx * g.block_m - g.group_padded_offsets[e];
+  const int rows = min(g.block_m, g.group_sizes[e] - row_in_group);
+  if (rows <= 0) return;
+  const int m_start = g.group_offsets[e] + row_in_group;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+
+  const int64_t kd = g.kd;
+  int col0;
+  const uint8_t* bptr[2];
+  float scale[2];
+  weight_rows<GATEUP, W8>(g, e, nt, wave, lr, lh, col0, bptr, scale);
+
+  const int nchunks = g.kd / kChunkK;
+  const int rot = 0;   // start of the reduction walk (chunk index rotation)
+  const int a_seg = tid & 7;    // 16-byte segment of a 128-byte A row chunk
+  const int a_row = tid >> 3;   // 0..31
+
+  for (int r0 = 0; r0 < rows; r0 += 32 * RG) {
+    const int rows_pass = min(32 * RG, rows - r0);
+    const int active = (rows_pass + 31) >> 5;
+
+    // A source row of each of this thread's row slots; slots past the
+    // block's rows re-read the pass's first row (in bounds, never stored).
+    const uint16_t* asrc[RG];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      int r = a_row + 32 * q;
+      if (r >= rows_pass) r = 0;
+      const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
+      asrc[q] = g.a + src * kd + a_seg * 8;
+    }
+    const int64_t out_row0 = m_start + r0;
+    if (active == RG) {
+      gemm_pass<DT, RG, RG, GATEUP, S, W8>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
+                                           a_seg, lr, lh, out_row0, rows_pass, col0);
+    } else if constexpr (RG == 2) {
+      gemm_pass<DT, 1, RG, GATEUP, S, W8>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
+                                          a_seg, lr, lh, out_row0, rows_pass, col0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide-block kernel for blocks of 128 or 256 rows (prefill-sized groups): the
+// layout of grouped_gemm_kernel (4 waves, each owning 32 columns of gate and
+// of up, or 64 of down, for ALL rows of the block; weights streamed from HBM
+// straight into B-operand registers, so a block reads its expert's weights
+// once) with the block's A rows staged by direct-to-LDS loads
+// (global_load_lds_dwordx4) instead of through registers. That frees the
+// registers for up to NAMAX = 6 row groups of accumulators (192 rows: a
+// whole prefill-sized expert group in one pass) plus a deep weight ring, and
+// every A fragment read from LDS feeds two MFMAs.
+//
+// A stage holds the pass's rows as 8-row groups of 1 KB, one DMA instruction
+// each (lane L writes 16 bytes at L*16: row L/8 of the group, slot L%8).
+// Slot s of row r holds segment s ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2), so
+// the fragment reads of 16 consecutive rows at one segment touch 16
+// different (row parity, slot) pairs: distinct banks whether the LDS serves
+// 8 lanes x 16 B or 16 lanes x 16 B per clock. Row group q of a chunk (32
+// rows = 4 DMA groups) is loaded by the 4 waves, one group each.
+//
+// Pipeline: the loads of chunk c+S-1 (A by DMA, B into registers) are issued
+// while chunk c is multiplied, so S-1 chunks of weights are in flight (S = 6:
+// 160 KB per CU). Each step waits (vmcnt) for this wave's loads of chunk c,
+// then meets the other waves at a plain s_barrier (no fence: a workgroup
+// fence would wait for every DMA load in flight), and only then issues chunk
+// c+S-1 into the stage and register slot that chunk c-1 used, which every
+// wave finished reading before the barrier (its MFMAs consumed the reads).
+// S need not divide the chunk count: full groups of S steps run while every
+// step's prefetch exists, and the last S..2S-1 chunks run as a guarded tail.
+constexpr int kAGroupElems = 8 * kChunkK;   // one 8-row DMA group: 1 KB
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's vector loads but the newest N
+// are complete, and so are its LDS accesses (the A tile it staged must be
+// written before the barrier that publishes it).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14], expcnt [6:4] (7 = no
+  // wait), lgkmcnt [11:8] (0 = wait for all).
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most `after` chunks of `ops` loads each are outstanding
+// (s_waitcnt takes an immediate: one case per possible count).
+template <int OPS, int MAXAFTER>
+__device__ __forceinline__ void wait_chunks_after(int after) {
+  static_for<MAXAFTER + 1>([&](auto I) {
+    constexpr int k = decltype(I)::value;
+    if (after == k) wait_vmcnt<(k * OPS < 63 ? k * OPS : 63)>();
+  });
+}
+
+// Register-staged variant of wide_pass: the A share of chunk c+S-1 is loaded
+// into registers together with its weights (A first), and written to a
+// double-buffered LDS tile at the end of step c+S-2, one step before it is
+// multiplied. Since vector loads complete in issue order, waiting for an A
+// share never waits for the weights issued after it, so S-1 chunks of
+// weights stay in flight. Same LDS row layout as the DMA variant (this
+// thread writes the 16 bytes the DMA lane would have written).
+template <int DT, int NA, bool GATEUP, int S, int NAMAX, bool W8>
+__device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
+                                          const uint16_t* const* a_src,
+                                          const uint8_t* const* bptr, const float* scale,
+                                          int nchunks, int wave, int lane, int lr, int lh,
+                                          int64_t out_row0, int rows, int col0) {
+  constexpr int kStage = NAMAX * 4 * kAGroupElems;
+  constexpr int kB = 2 * BChunk<DT, W8>::kVec;   // weight loads per chunk per wave
+  constexpr int kOps = NA + kB;                   // vector memory ops per chunk per wave
+  f32x16 acc[NA][2];
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+    acc[q][0] = f32x16{};
+    acc[q][1] = f32x16{};
+  }
+  BChunk<DT, W8> bring[S];
+  u32x4 aring[S][NA];
+
+  auto load_chunk = [&](int c, int slot) {
+    const int64_t off = static_cast<int64_t>(c) * kChunkK;
+#pragma unroll
+    for (int q = 0; q < NA; ++q) aring[slot][q] = load16(a_src[q] + off);
+    bring[slot].load(bptr, off);
+  };
+  // Write chunk c's A share (ring slot `slot`) into LDS buffer c % 2.
+  auto stage_a = [&](int c, int slot) {
+    uint16_t* stage = lds_ring + (c & 1) * kStage + wave * kAGroupElems + lane * 8;
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      *reinterpret_cast<u32x4*>(stage + q * 4 * kAGroupElems) = aring[slot][q];
+    }
+  };
+
+  const int f_row = (lr & 7) ^ ((lr >> 3) & 1);
+  const int row_off = (lr >> 3) * kAGroupElems + (lr & 7) * kChunkK;
+  auto multiply = [&](int c, auto U) {
+    constexpr int u = decltype(U)::value % S;
+    const uint16_t* stage = lds_ring + (c & 1) * kStage + row_off;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int slot = (lh * 4 + t) ^ f_row;
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(stage + q * 4 * kAGroupElems + slot * 8);
+        acc[q][0] = mfma32x32x16<DT>(a, bring[u].operand(0, t), acc[q][0]);
+        acc[q][1] = mfma32x32x16<DT>(a, bring[u].operand(1, t), acc[q][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Prologue: chunks 0..S-2 in flight; stage chunk 0's A share.
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) load_chunk(st, st);
+  wait_vmcnt<(kB + (S - 2) * kOps < 63 ? kB + (S - 2) * kOps : 63)>();
+  stage_a(0, 0);
+
+  // Step c: wait for chunk c's weights, barrier (chunk c's A share is in
+  // LDS; every wave is done with buffer (c+1) % 2), prefetch chunk c+S-1,
+  // multiply chunk c, then wait for chunk c+1's A share and stage it.
+  int c0 = 0;
+  for (; c0 + 2 * S - 1 <= nchunks - 1; c0 += S) {
+    static_for<S>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      wait_vmcnt<(S - 2) * kOps>();
+      __builtin_amdgcn_s_barrier();
+      load_chunk(c0 + u + S - 1, (u + S - 1) % S);
+      multiply(c0 + u, U);
+      wait_vmcnt<(kB + (S - 2) * kOps < 63 ? kB + (S - 2) * kOps : 63)>();
+      stage_a(c0 + u + 1, (u + 1) % S);
+    });
+  }
+  // Tail: the last R chunks, S <= R < 2S.
+  const int rem = nchunks - c0;
+  static_for<2 * S>([&](auto U) {
+    constexpr int u = decltype(U)::value;
+    if (u < rem) {
+      wait_chunks_after<kOps, S - 2>(min(S - 2, rem - 1 - u));
+      __builtin_amdgcn_s_barrier();
+      if (u + S - 1 < rem) load_chunk(c0 + u + S - 1, (u + S - 1) % S);
+      multiply(c0 + u, U);
+      if (u + 1 < rem) {
+        // Chunks issued after chunk c+1: up to min(c+S-1, n-1).
+        const int after = min(S - 2, rem - 2 - u);
+        static_for<S - 1>([&](auto I) {
+          constexpr int k = decltype(I)::value;
+          if (after == k) wait_vmcnt<(kB + k * kOps < 63 ? kB + k * kOps : 63)>();
+        });
+        stage_a(c0 + u + 1, (u + 1) % S);
+      }
+    }
+  });
+
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = q * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+      if (row < rows) {
+        uint16_t* out = g.c + (out_row0 + row) * g.n + col0 + lr;
+        float v0 = acc[q][0][i], v1 = acc[q][1][i];
+        if constexpr (W8) {   // the rows' scales, once per dot product
+          v0 *= scale[0];
+          v1 *= scale[1];
+        }
+        if constexpr (GATEUP) {
+          out[0] = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
+        } else {
+          out[0] = static_cast<uint16_t>(from_float<DT>(v0));
+          out[32] = static_cast<uint16_t>(from_float<DT>(v1));
+        }
+      }
+    }
+  }
+}
+
+template <int DT, bool GATEUP, int S, int NAMAX, bool W8>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_ring[2 * NAMAX * 4 * kAGroupElems];
+
+  const int total = g.active_count[0] * g.n_tiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
+  const int ab = natural / g.n_tiles;
+  const int nt = natural - ab * g.n_tiles;
+  const int bx = g.active_blocks[ab];
+
+  const int e = g.block_expert[bx];
+  const int row_in_group = bx * g.block_m - g.group_padded_offsets[e];
+  const int rows = min(g.block_m, g.group_sizes[e] - row_in_group);
+  if (rows <= 0) return;
+  const int m_start = g.group_offsets[e] + row_in_group;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int64_t kd = g.kd;
+  const int nchunks = g.kd / kChunkK;
+
+  int col0;
+  const uint8_t* bptr[2];
+  float scale[2];
+  weight_rows<GATEUP, W8>(g, e, nt, wave, lr, lh, col0, bptr, scale);
+
+  // One pass over the weights covers up to NAMAX row groups; a block with
+  // more rows (at most 8 groups) takes two balanced passes of up to 4 groups
+  // (written out rather than as a loop, so the register allocation of the
+  // large pass is not burdened by the loop).
+  auto run_pass = [&](int r0, auto NAP) {
+    constexpr int kMaxNa = decltype(NAP)::value;
+    const int rows_pass = min(32 * kMaxNa, rows - r0);
+    // This lane's DMA source for row group q: row 32q + 8*wave + lane/8 of
+    // the pass (row 0 of the pass past its rows: in bounds, never stored),
+    // segment (lane % 8) ^ f(row) with f(row) = (lane / 8) ^ (wave % 2).
+    const uint16_t* a_src[kMaxNa];
+    const int seg = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+#pragma unroll
+    for (int q = 0; q < kMaxNa; ++q) {
+      int r = 32 * q + 8 * wave + (lane >> 3);
+      if (r >= rows_pass) r = 0;
+      const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
+      a_src[q] = g.a + src * kd + seg * 8;
+    }
+    const int active = (rows_pass + 31) >> 5;
+    static_for<kMaxNa>([&](auto I) {
+      constexpr int na = decltype(I)::value + 1;
+      if (active == na) {
+        wide_pass<DT, na, GATEUP, S, NAMAX, W8>(g, lds_ring, a_src, bptr, scale, nchunks, wave,
+                                                lane, lr, lh, m_start + r0, rows_pass, col0);
+      }
+    });
+  };
+  if (rows <= 32 * NAMAX) {
+    run_pass(0, int_c<NAMAX>{});
+  } else {
+    run_pass(0, int_c<4>{});
+    __builtin_amdgcn_s_barrier();   // every wave is done with the LDS tile
+    run_pass(128, int_c<4>{});
+  }
+}
+
+template <int DT, bool GATEUP, int NAMAX, bool W8>
+void launch_wide(unsigned grid, const GemmArgs& g, hipStream_t stream) {
+  // Depth S needs at least S chunks; a 128-long reduction (the shortest the
+  // shape rules allow: 2 chunks) runs at depth 2. FP8 weight chunks take
+  // half the registers, so they run deeper (5).
+  constexpr int S = W8 ? 5 : kStagesWide;
+  if (g.kd / kChunkK >= S) {
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<DT, GATEUP, S, NAMAX, W8>), dim3(grid),
+                       dim3(kThreads), 0, stream, g);
+  } else {
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<DT, GATEUP, 2, NAMAX, W8>), dim3(grid),
+                       dim3(kThreads), 0, stream, g);
+  }
+}
+
+template <int DT, int RG, bool GATEUP, int S, bool W8>
+void launch_rg(unsigned grid, const GemmArgs& g, hipStream_t stream) {
+  // Depth S needs at least S chunks (kd / 64; >= 2 by the shape rules);
+  // fall back to depth 2 below that.
+  if (g.kd / kChunkK >= S) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<DT, RG, GATEUP, S, W8>), dim3(grid), dim3(kThreads),
+                       0, stream, g);
+  } else {
+    hipLaunchKernelGGL((grouped_gemm_kernel<DT, RG, GATEUP, 2, W8>), dim3(grid), dim3(kThreads),
+                       0, stream, g);
+  }
+}
+
+// Both grouped GEMMs for activation dtype DT (bf16 / fp16) and weights of
+// the same dtype or, with W8, FP8 E4M3 codes with per-row scales.
+template <int DT, bool GATEUP, bool W8>
+hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  GemmArgs g;
+  g.a = static_cast<const uint16_t*>(p.a);
+  g.b0 = p.b0;
+  g.b1 = p.b1;
+  g.s0 = p.s0;
+  g.s1 = p.s1;
+  g.c = static_cast<uint16_t*>(p.c);
+  g.sorted_token = t.sorted_token;
+  g.group_sizes = t.group_sizes;
+  g.group_offsets = t.group_offsets;
+  g.group_padded_offsets = t.group_padded_offsets;
+  g.block_expert = t.block_expert;
+  g.active_blocks = t.active_blocks;
+  g.active_count = t.active_count;
+  g.n = p.n;
+  g.kd = p.kd;
+  g.block_m = t.block_m;
+  // Blocks of <= 64 rows: grouped_gemm_kernel (128 h columns or 256 output
+  // columns per workgroup); 128- and 256-row blocks: the wide kernel (same
+  // column tiles).
+  g.n_tiles = p.n / (GATEUP ? 128 : 256);
+  const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
+  const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
+  if (t.block_m <= 32) {
+    // FP8 weight chunks take half the registers: depth 6 for both GEMMs,
+    // still two workgroups per CU.
+    constexpr int S = W8 ? MOE_W8_RG1_STAGES : (GATEUP ? kStagesRG1 : kStagesRG1Down);
+    launch_rg<DT, 1, GATEUP, S, W8>(grid, g, stream);
+  } else if (t.block_m == 64) {
+    launch_rg<DT, 2, GATEUP, kStagesRG2, W8>(grid, g, stream);
+  } else if (t.block_m == 128) {
+    launch_wide<DT, GATEUP, 4, W8>(grid, g, stream);
+  } else {
+    launch_wide<DT, GATEUP, 6, W8>(grid, g, stream);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+}  // namespace moe

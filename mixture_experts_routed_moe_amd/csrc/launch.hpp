@@ -21,10 +21,17 @@ struct GemmProblem {
   int n;                 // output columns (D for gate/up, H for down)
   int kd;                // reduction length (H for gate/up, D for down)
   int dtype;             // kF16 / kBF16 / kF32
+  const float* s0 = nullptr;   // FP8 weights: fp32 scale per row of b0
+  const float* s1 = nullptr;   // FP8 weights: fp32 scale per row of b1
 };
 
 hipError_t launch_gate_up(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+// FP8 E4M3 weights (b0 / b1 hold codes; s0 / s1 the per-row scales).
+hipError_t launch_gate_up_w8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_down_w8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_quantize_fp8_rows(const void* w, int64_t rows, int cols, int dtype, uint8_t* q,
+                                    float* scales, hipStream_t stream);
 hipError_t launch_gate_up_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 

@@ -1,0 +1,63 @@
+// Per-row FP8 E4M3 quantisation of expert weights (the FP8 weight format of
+// grouped_gemm_w8.hip): for each row r of `cols` values,
+//   amax = max_k |w[r, k]|,  s[r] = amax / 448 (1 for an all-zero row),
+//   q[r, k] = FP8(w[r, k] / s[r])  (fp32 division, correctly rounded; round
+//                                    to nearest even, saturating at +-448).
+// One wave per row: a strided pass for the wave-wide maximum, a second pass
+// (served by the cache: a row is at most a few tens of KB) for the codes. A
+// one-time conversion of the stacked weights, not on the forward path.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+template <int DT>
+__device__ __forceinline__ float load_w(const void* w, int64_t i) {
+  if constexpr (DT == kF32) {
+    return static_cast<const float*>(w)[i];
+  } else {
+    return to_float<DT>(static_cast<const uint16_t*>(w)[i]);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_fp8_rows_kernel(const void* __restrict__ w,
+                                                                int64_t rows, int cols,
+                                                                uint8_t* __restrict__ q,
+                                                                float* __restrict__ scales) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;                 // whole wave exits together
+  const int lane = threadIdx.x & 63;
+  const int64_t base = r * cols;
+  float amax = 0.0f;
+  for (int k = lane; k < cols; k += 64) amax = fmaxf(amax, fabsf(load_w<DT>(w, base + k)));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (lane == 0) scales[r] = s;
+  for (int k = lane; k < cols; k += 64) {
+    q[base + k] = static_cast<uint8_t>(float_to_fp8e4m3(load_w<DT>(w, base + k) / s));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8_rows(const void* w, int64_t rows, int cols, int dtype, uint8_t* q,
+                                    float* scales, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (dtype == kBF16) {
+    hipLaunchKernelGGL(quantize_fp8_rows_kernel<kBF16>, grid, dim3(256), 0, stream, w, rows, cols,
+                       q, scales);
+  } else if (dtype == kF16) {
+    hipLaunchKernelGGL(quantize_fp8_rows_kernel<kF16>, grid, dim3(256), 0, stream, w, rows, cols,
+                       q, scales);
+  } else {
+    hipLaunchKernelGGL(quantize_fp8_rows_kernel<kF32>, grid, dim3(256), 0, stream, w, rows, cols,
+                       q, scales);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe
