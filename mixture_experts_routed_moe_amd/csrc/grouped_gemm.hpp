@@ -71,7 +71,10 @@ constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
 // kernel runs at depth 4 (registers: 6 row groups of accumulators, the
 // weight ring and the A ring fill the 512 registers of one wave per SIMD).
 #ifndef MOE_W8_RG1_STAGES
-#define MOE_W8_RG1_STAGES 6
+#define MOE_W8_RG1_STAGES 4
+#endif
+#ifndef MOE_W8_WIDE_STAGES
+#define MOE_W8_WIDE_STAGES 4
 #endif
 #ifndef MOE_RG1_DOWN_STAGES
 #define MOE_RG1_DOWN_STAGES 2
@@ -117,14 +120,16 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // One chunk of a wave's weights: for each of its two weight rows, the lane's
-// 32 reduction elements as loaded -- 16-bit values (4 x 16 bytes) or FP8 E4M3
-// codes (W8: 2 x 16 bytes) -- and their MFMA B operand for k-slice t (8
-// 16-bit values, elements 8t..8t+7 of the lane's 32). FP8 codes are decoded
+// CK/2 reduction elements as loaded -- 16-bit values (CK = 64: 4 x 16 bytes)
+// or FP8 E4M3 codes (W8: 2 x 16 bytes at CK = 64, 4 x 16 bytes at CK = 128)
+// -- and their MFMA B operand for k-slice t (8 16-bit values, elements
+// 8t..8t+7 of the lane's CK/2). FP8 codes are decoded
 // to the activation dtype, exactly (every E4M3 value is a bf16 and an fp16
 // value), two per v_cvt_scalef32_pk instruction with scale 1.
-template <int DT, bool W8>
+template <int DT, bool W8, int CK = kChunkK>
 struct BChunk {
-  static constexpr int kVec = W8 ? 2 : 4;
+  // 16-byte loads per row: the lane's CK/2 elements of 1 or 2 bytes.
+  static constexpr int kVec = (CK / 2) * (W8 ? 1 : 2) / 16;
   u32x4 v[2][kVec];
 
   // p: the lane's two row pointers (byte addresses); off: reduction offset.
@@ -179,8 +184,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // The two weight rows a lane streams and their scales: gate/up -- row col0
 // + lane%32 of W_gate and of W_up (col0 = 128*nt + 32*wave); down -- rows
 // col0 + lane%32 and col0 + 32 + lane%32 of W_down (col0 = 256*nt +
-// 64*wave). The lane starts at reduction element 32*(lane/32) of each row.
-template <bool GATEUP, bool W8>
+// 64*wave). The lane starts at reduction element (CK/2)*(lane/32) of each
+// row (CK: reduction elements per chunk).
+template <bool GATEUP, bool W8, int CK = kChunkK>
 __device__ __forceinline__ void weight_rows(const GemmArgs& g, int e, int nt, int wave, int lr,
                                             int lh, int& col0, const uint8_t** bptr,
                                             float* scale) {
@@ -199,8 +205,8 @@ __device__ __forceinline__ void weight_rows(const GemmArgs& g, int e, int nt, in
   }
   const uint8_t* b0 = static_cast<const uint8_t*>(g.b0);
   const uint8_t* b1 = static_cast<const uint8_t*>(GATEUP ? g.b1 : g.b0);
-  bptr[0] = b0 + (row[0] * kd + lh * 32) * eb;
-  bptr[1] = b1 + (row[1] * kd + lh * 32) * eb;
+  bptr[0] = b0 + (row[0] * kd + lh * (CK / 2)) * eb;
+  bptr[1] = b1 + (row[1] * kd + lh * (CK / 2)) * eb;
   if constexpr (W8) {
     scale[0] = g.s0[row[0]];
     scale[1] = (GATEUP ? g.s1 : g.s0)[row[1]];
@@ -218,8 +224,8 @@ __device__ __forceinline__ void weight_rows(const GemmArgs& g, int e, int nt, in
 // flight across the per-chunk barrier. The loop body is straight-line (no
 // branch touches the accumulators, so they stay in place); the last chunks
 // run as a guarded tail without prefetches past the end.
-template <int DT, int NA, int RG, bool GATEUP, int S, bool W8>
-__device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[32 * RG][kLdsRow],
+template <int DT, int NA, int RG, bool GATEUP, int S, bool W8, int CK>
+__device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[32 * RG][CK + 8],
                                           const uint16_t* const* asrc,
                                           const uint8_t* const* bptr, const float* scale,
                                           int nchunks, int rot, int a_row, int a_seg, int lr,
@@ -230,23 +236,37 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
     acc[q][0] = f32x16{};
     acc[q][1] = f32x16{};
   }
-  u32x4 aring[S][NA];
-  BChunk<DT, W8> bring[S];
+  // A rows per pass of the 256 threads over a chunk (one 16-byte segment
+  // each): 32 at CK = 64, 16 at CK = 128 (then kSub = 2 rows per thread and
+  // row group).
+  constexpr int kARows = 256 / (CK / 8);
+  constexpr int kSub = 32 / kARows;
+  u32x4 aring[S][NA][kSub];
+  BChunk<DT, W8, CK> bring[S];
 
   auto load_chunk = [&](int c, int slot) {
     int cc = c + rot;
     if (cc >= nchunks) cc -= nchunks;
-    const int64_t off = static_cast<int64_t>(cc) * kChunkK;
+    const int64_t off = static_cast<int64_t>(cc) * CK;
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
-      if (a_row + 32 * q < rows_pass) aring[slot][q] = load16(asrc[q] + off);
+#pragma unroll
+      for (int sb = 0; sb < kSub; ++sb) {
+        if (a_row + kARows * sb + 32 * q < rows_pass) {
+          aring[slot][q][sb] = load16(asrc[q * kSub + sb] + off);
+        }
+      }
     }
     bring[slot].load(bptr, off);
   };
   auto stage_a = [&](int slot, int buf) {
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
-      if (a_row + 32 * q < rows_pass) *reinterpret_cast<u32x4*>(&lds_a[buf][a_row + 32 * q][a_seg * 8]) = aring[slot][q];
+#pragma unroll
+      for (int sb = 0; sb < kSub; ++sb) {
+        const int r = a_row + kARows * sb + 32 * q;
+        if (r < rows_pass) *reinterpret_cast<u32x4*>(&lds_a[buf][r][a_seg * 8]) = aring[slot][q][sb];
+      }
     }
   };
 
@@ -264,11 +284,11 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
     if (prefetch) load_chunk(c + S - 1, (u + S - 1) % S);
     constexpr int buf = u & 1;   // S is even, so c & 1 == u & 1
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < CK / 16; ++t) {
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
         const u32x4 a =
-            *reinterpret_cast<const u32x4*>(&lds_a[buf][q * 32 + lr][lh * 32 + t * 8]);
+            *reinterpret_cast<const u32x4*>(&lds_a[buf][q * 32 + lr][lh * (CK / 2) + t * 8]);
         acc[q][0] = mfma32x32x16<DT>(a, bring[u].operand(0, t), acc[q][0]);
         acc[q][1] = mfma32x32x16<DT>(a, bring[u].operand(1, t), acc[q][1]);
       }
@@ -319,7 +339,11 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
 // wave, contiguous A); S = software-pipeline depth in chunks.
 template <int DT, int RG, bool GATEUP, int S, bool W8>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][32 * RG][kLdsRow];
+  // Reduction elements per chunk: 64; 128 with FP8 weights, so a lane still
+  // loads 64 contiguous bytes of each weight row per chunk (two lanes cover
+  // a 128-byte segment) and the A rows of a chunk are 256 bytes.
+  constexpr int CK = W8 ? 128 : kChunkK;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][32 * RG][CK + 8];
 
   // Only blocks that hold rows are scheduled: the grid is sized for every
   // block, and workgroups past the active work exit at once.
@@ -347,12 +371,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   int col0;
   const uint8_t* bptr[2];
   float scale[2];
-  weight_rows<GATEUP, W8>(g, e, nt, wave, lr, lh, col0, bptr, scale);
+  weight_rows<GATEUP, W8, CK>(g, e, nt, wave, lr, lh, col0, bptr, scale);
 
-  const int nchunks = g.kd / kChunkK;
+  const int nchunks = g.kd / CK;
   const int rot = 0;   // start of the reduction walk (chunk index rotation)
-  const int a_seg = tid & 7;    // 16-byte segment of a 128-byte A row chunk
-  const int a_row = tid >> 3;   // 0..31
+  constexpr int kASeg = CK / 8;             // 16-byte segments of an A row chunk
+  constexpr int kARows = 256 / kASeg;       // A rows per pass of the threads
+  constexpr int kSub = 32 / kARows;
+  const int a_seg = tid % kASeg;
+  const int a_row = tid / kASeg;
 
   for (int r0 = 0; r0 < rows; r0 += 32 * RG) {
     const int rows_pass = min(32 * RG, rows - r0);
@@ -360,20 +387,23 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
 
     // A source row of each of this thread's row slots; slots past the
     // block's rows re-read the pass's first row (in bounds, never stored).
-    const uint16_t* asrc[RG];
+    const uint16_t* asrc[RG * kSub];
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
-      int r = a_row + 32 * q;
-      if (r >= rows_pass) r = 0;
-      const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
-      asrc[q] = g.a + src * kd + a_seg * 8;
+#pragma unroll
+      for (int sb = 0; sb < kSub; ++sb) {
+        int r = a_row + kARows * sb + 32 * q;
+        if (r >= rows_pass) r = 0;
+        const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
+        asrc[q * kSub + sb] = g.a + src * kd + a_seg * 8;
+      }
     }
     const int64_t out_row0 = m_start + r0;
     if (active == RG) {
-      gemm_pass<DT, RG, RG, GATEUP, S, W8>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
+      gemm_pass<DT, RG, RG, GATEUP, S, W8, CK>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
                                            a_seg, lr, lh, out_row0, rows_pass, col0);
     } else if constexpr (RG == 2) {
-      gemm_pass<DT, 1, RG, GATEUP, S, W8>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
+      gemm_pass<DT, 1, RG, GATEUP, S, W8, CK>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
                                           a_seg, lr, lh, out_row0, rows_pass, col0);
     }
   }
@@ -627,7 +657,7 @@ void launch_wide(unsigned grid, const GemmArgs& g, hipStream_t stream) {
   // Depth S needs at least S chunks; a 128-long reduction (the shortest the
   // shape rules allow: 2 chunks) runs at depth 2. FP8 weight chunks take
   // half the registers, so they run deeper (5).
-  constexpr int S = W8 ? 5 : kStagesWide;
+  constexpr int S = W8 ? MOE_W8_WIDE_STAGES : kStagesWide;
   if (g.kd / kChunkK >= S) {
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<DT, GATEUP, S, NAMAX, W8>), dim3(grid),
                        dim3(kThreads), 0, stream, g);
@@ -639,9 +669,10 @@ void launch_wide(unsigned grid, const GemmArgs& g, hipStream_t stream) {
 
 template <int DT, int RG, bool GATEUP, int S, bool W8>
 void launch_rg(unsigned grid, const GemmArgs& g, hipStream_t stream) {
-  // Depth S needs at least S chunks (kd / 64; >= 2 by the shape rules);
-  // fall back to depth 2 below that.
-  if (g.kd / kChunkK >= S) {
+  // Depth S needs at least S chunks (kd / 64, or kd / 128 with FP8 weights;
+  // >= 1 by the shape rules); fall back to depth 2 below that (a single
+  // chunk runs the tail alone).
+  if (g.kd / (W8 ? 128 : kChunkK) >= S) {
     hipLaunchKernelGGL((grouped_gemm_kernel<DT, RG, GATEUP, S, W8>), dim3(grid), dim3(kThreads),
                        0, stream, g);
   } else {
@@ -678,8 +709,8 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
   const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
   const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
   if (t.block_m <= 32) {
-    // FP8 weight chunks take half the registers: depth 6 for both GEMMs,
-    // still two workgroups per CU.
+    // FP8 weights: 128-element chunks of the same bytes per row as the
+    // 16-bit chunks, depth 4 for both GEMMs.
     constexpr int S = W8 ? MOE_W8_RG1_STAGES : (GATEUP ? kStagesRG1 : kStagesRG1Down);
     launch_rg<DT, 1, GATEUP, S, W8>(grid, g, stream);
   } else if (t.block_m == 64) {
