@@ -82,7 +82,13 @@ constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
 constexpr int kStagesRG1 = 4;
 constexpr int kStagesRG1Down = MOE_RG1_DOWN_STAGES;
 constexpr int kStagesRG2 = 4;
-constexpr int kStagesWide = 4;
+#ifndef MOE_WIDE_STAGES
+#define MOE_WIDE_STAGES 4
+#endif
+#ifndef MOE_WIDE_NAMAX
+#define MOE_WIDE_NAMAX 6
+#endif
+constexpr int kStagesWide = MOE_WIDE_STAGES;
 
 struct GemmArgs {
   const uint16_t* a;
@@ -244,7 +250,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
   u32x4 aring[S][NA][kSub];
   BChunk<DT, W8, CK> bring[S];
 
-  auto load_chunk = [&](int c, int slot) {
+  auto load_chunk = [&](int c, int slot) __attribute__((always_inline)) {
     int cc = c + rot;
     if (cc >= nchunks) cc -= nchunks;
     const int64_t off = static_cast<int64_t>(cc) * CK;
@@ -259,7 +265,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
     }
     bring[slot].load(bptr, off);
   };
-  auto stage_a = [&](int slot, int buf) {
+  auto stage_a = [&](int slot, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
 #pragma unroll
@@ -279,7 +285,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
   // end is ever loaded), multiply chunk c, stage chunk c+1's A share,
   // barrier. U = c % S (the register slot).
   static_assert(S % 2 == 0, "the LDS buffer of chunk c is c % 2 == slot % 2");
-  auto step = [&](int c, auto U, bool prefetch, bool stage) {
+  auto step = [&](int c, auto U, bool prefetch, bool stage) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
     if (prefetch) load_chunk(c + S - 1, (u + S - 1) % S);
     constexpr int buf = u & 1;   // S is even, so c & 1 == u & 1
@@ -414,30 +420,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
 // layout of grouped_gemm_kernel (4 waves, each owning 32 columns of gate and
 // of up, or 64 of down, for ALL rows of the block; weights streamed from HBM
 // straight into B-operand registers, so a block reads its expert's weights
-// once) with the block's A rows staged by direct-to-LDS loads
-// (global_load_lds_dwordx4) instead of through registers. That frees the
-// registers for up to NAMAX = 6 row groups of accumulators (192 rows: a
-// whole prefill-sized expert group in one pass) plus a deep weight ring, and
-// every A fragment read from LDS feeds two MFMAs.
+// once) with up to NAMAX = 6 row groups of accumulators (192 rows: a whole
+// prefill-sized expert group in one pass). Every A fragment read from LDS
+// feeds two MFMAs.
 //
-// A stage holds the pass's rows as 8-row groups of 1 KB, one DMA instruction
-// each (lane L writes 16 bytes at L*16: row L/8 of the group, slot L%8).
-// Slot s of row r holds segment s ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2), so
-// the fragment reads of 16 consecutive rows at one segment touch 16
-// different (row parity, slot) pairs: distinct banks whether the LDS serves
-// 8 lanes x 16 B or 16 lanes x 16 B per clock. Row group q of a chunk (32
-// rows = 4 DMA groups) is loaded by the 4 waves, one group each.
+// A stage holds the pass's rows as 8-row groups of 1 KB (the 16 bytes of
+// thread L of a wave: row L/8 of the group, slot L%8). Slot s of row r holds
+// segment s ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2), so the fragment reads of
+// 16 consecutive rows at one segment touch 16 different (row parity, slot)
+// pairs: distinct banks whether the LDS serves 8 lanes x 16 B or 16 lanes x
+// 16 B per clock. Row group q of a chunk (32 rows = 4 groups of 8) is written
+// by the 4 waves, one group each.
 //
-// Pipeline: the loads of chunk c+S-1 (A by DMA, B into registers) are issued
-// while chunk c is multiplied, so S-1 chunks of weights are in flight (S = 6:
-// 160 KB per CU). Each step waits (vmcnt) for this wave's loads of chunk c,
-// then meets the other waves at a plain s_barrier (no fence: a workgroup
-// fence would wait for every DMA load in flight), and only then issues chunk
-// c+S-1 into the stage and register slot that chunk c-1 used, which every
-// wave finished reading before the barrier (its MFMAs consumed the reads).
-// S need not divide the chunk count: full groups of S steps run while every
-// step's prefetch exists, and the last S..2S-1 chunks run as a guarded tail.
-constexpr int kAGroupElems = 8 * kChunkK;   // one 8-row DMA group: 1 KB
+// Pipeline: the loads of chunk c+S-1 (A share and weights, into registers)
+// are issued while chunk c is multiplied, so S-1 chunks of weights are in
+// flight. Each step waits (vmcnt) for this wave's weights of chunk c, then
+// meets the other waves at a plain s_barrier (chunk c's A tile is complete
+// in LDS), issues chunk c+S-1 into the register slot that chunk c-1 used,
+// multiplies chunk c, and writes chunk c+1's A share into the other LDS
+// buffer (which every wave finished reading before the barrier). S need not
+// divide the chunk count: full groups of S steps run while every step's
+// prefetch exists, and the last S..2S-1 chunks run as a guarded tail.
+constexpr int kAGroupElems = 8 * kChunkK;   // one 8-row group of a stage: 1 KB
 
 // s_waitcnt vmcnt(N) lgkmcnt(0): this wave's vector loads but the newest N
 // are complete, and so are its LDS accesses (the A tile it staged must be
@@ -460,13 +464,12 @@ __device__ __forceinline__ void wait_chunks_after(int after) {
   });
 }
 
-// Register-staged variant of wide_pass: the A share of chunk c+S-1 is loaded
-// into registers together with its weights (A first), and written to a
-// double-buffered LDS tile at the end of step c+S-2, one step before it is
-// multiplied. Since vector loads complete in issue order, waiting for an A
-// share never waits for the weights issued after it, so S-1 chunks of
-// weights stay in flight. Same LDS row layout as the DMA variant (this
-// thread writes the 16 bytes the DMA lane would have written).
+// One pass of the wide kernel over the reduction for NA row groups: the A
+// share of chunk c+S-1 is loaded into registers together with its weights (A
+// first), and written to a double-buffered LDS tile at the end of step
+// c+S-2, one step before it is multiplied. Since vector loads complete in
+// issue order, waiting for an A share never waits for the weights issued
+// after it, so S-1 chunks of weights stay in flight.
 template <int DT, int NA, bool GATEUP, int S, int NAMAX, bool W8>
 __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
                                           const uint16_t* const* a_src,
@@ -485,14 +488,14 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
   BChunk<DT, W8> bring[S];
   u32x4 aring[S][NA];
 
-  auto load_chunk = [&](int c, int slot) {
+  auto load_chunk = [&](int c, int slot) __attribute__((always_inline)) {
     const int64_t off = static_cast<int64_t>(c) * kChunkK;
 #pragma unroll
     for (int q = 0; q < NA; ++q) aring[slot][q] = load16(a_src[q] + off);
     bring[slot].load(bptr, off);
   };
   // Write chunk c's A share (ring slot `slot`) into LDS buffer c % 2.
-  auto stage_a = [&](int c, int slot) {
+  auto stage_a = [&](int c, int slot) __attribute__((always_inline)) {
     uint16_t* stage = lds_ring + (c & 1) * kStage + wave * kAGroupElems + lane * 8;
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
@@ -502,26 +505,41 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
 
   const int f_row = (lr & 7) ^ ((lr >> 3) & 1);
   const int row_off = (lr >> 3) * kAGroupElems + (lr & 7) * kChunkK;
-  auto multiply = [&](int c, auto U) {
+  // Multiply chunk c: A fragments are read one k-slice ahead, so slice
+  // t+1's LDS reads are in flight during slice t's MFMAs.
+  auto multiply = [&](int c, auto U) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value % S;
     const uint16_t* stage = lds_ring + (c & 1) * kStage + row_off;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    u32x4 af[2][NA];
+    auto read_a = [&](int t, int b) __attribute__((always_inline)) {
       const int slot = (lh * 4 + t) ^ f_row;
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(stage + q * 4 * kAGroupElems + slot * 8);
-        acc[q][0] = mfma32x32x16<DT>(a, bring[u].operand(0, t), acc[q][0]);
-        acc[q][1] = mfma32x32x16<DT>(a, bring[u].operand(1, t), acc[q][1]);
+        af[b][q] = *reinterpret_cast<const u32x4*>(stage + q * 4 * kAGroupElems + slot * 8);
+      }
+    };
+    read_a(0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < 3) read_a(t + 1, (t + 1) & 1);
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        acc[q][0] = mfma32x32x16<DT>(af[t & 1][q], bring[u].operand(0, t), acc[q][0]);
+        acc[q][1] = mfma32x32x16<DT>(af[t & 1][q], bring[u].operand(1, t), acc[q][1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Prologue: chunks 0..S-2 in flight; stage chunk 0's A share.
+  // Prologue: chunks 0..S-2 in flight; stage chunk 0's A share. The loads
+  // keep the loop's order (chunk by chunk, A before B): the compiler's own
+  // load counting at the loop head merges this path with the back edge, and
+  // a different order here would make it wait for far more than needed.
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st) load_chunk(st, st);
+  for (int st = 0; st < S - 1; ++st) {
+    load_chunk(st, st);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   wait_vmcnt<(kB + (S - 2) * kOps < 63 ? kB + (S - 2) * kOps : 63)>();
   stage_a(0, 0);
 
@@ -618,11 +636,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
   // One pass over the weights covers up to NAMAX row groups; a block with
   // more rows (at most 8 groups) takes two balanced passes of up to 4 groups
   // (written out rather than as a loop, so the register allocation of the
-  // large pass is not burdened by the loop).
-  auto run_pass = [&](int r0, auto NAP) {
+  // large pass is not burdened by the loop). Every lambda here is forced
+  // inline: an outlined pass (the compiler's choice when the same pass is
+  // called three times) goes through a call with its arguments in scratch.
+  auto run_pass = [&](int r0, auto NAP) __attribute__((always_inline)) {
     constexpr int kMaxNa = decltype(NAP)::value;
     const int rows_pass = min(32 * kMaxNa, rows - r0);
-    // This lane's DMA source for row group q: row 32q + 8*wave + lane/8 of
+    // This lane's A source for row group q: row 32q + 8*wave + lane/8 of
     // the pass (row 0 of the pass past its rows: in bounds, never stored),
     // segment (lane % 8) ^ f(row) with f(row) = (lane / 8) ^ (wave % 2).
     const uint16_t* a_src[kMaxNa];
@@ -655,8 +675,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
 template <int DT, bool GATEUP, int NAMAX, bool W8>
 void launch_wide(unsigned grid, const GemmArgs& g, hipStream_t stream) {
   // Depth S needs at least S chunks; a 128-long reduction (the shortest the
-  // shape rules allow: 2 chunks) runs at depth 2. FP8 weight chunks take
-  // half the registers, so they run deeper (5).
+  // shape rules allow: 2 chunks) runs at depth 2.
   constexpr int S = W8 ? MOE_W8_WIDE_STAGES : kStagesWide;
   if (g.kd / kChunkK >= S) {
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<DT, GATEUP, S, NAMAX, W8>), dim3(grid),
@@ -718,7 +737,7 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
   } else if (t.block_m == 128) {
     launch_wide<DT, GATEUP, 4, W8>(grid, g, stream);
   } else {
-    launch_wide<DT, GATEUP, 6, W8>(grid, g, stream);
+    launch_wide<DT, GATEUP, MOE_WIDE_NAMAX, W8>(grid, g, stream);
   }
   return hipGetLastError();
 }
