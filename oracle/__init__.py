@@ -49,6 +49,11 @@ def lib():
         L.oracle_moe_forward_w8.argtypes = [i32, vp, vp, vp, vp, f32p, f32p, f32p, i32p, f32p,
                                             i32, i32, i32, i32, i32, i32p, i32, f32p, f32p, f32p]
         L.oracle_gate.argtypes = [i32, vp, f32p, f32p, i32, i32, i32, i32, i32, f32p, i32p, f32p]
+        L.oracle_quantize_int8_rows.argtypes = [i32, vp, i64, i32, vp, f32p]
+        L.oracle_quantize_int4_rows.argtypes = [i32, vp, i64, i32, vp, f32p]
+        L.oracle_w4a8_gemm.argtypes = [vp, vp, i32, i32, i32, vp]
+        L.oracle_moe_forward_w4a8.argtypes = [i32, vp, vp, vp, vp, f32p, f32p, f32p, i32p, f32p,
+                                              i32, i32, i32, i32, i32, i32p, i32, f32p, f32p, f32p]
         _lib = L
     return _lib
 
@@ -243,4 +248,67 @@ def moe_forward_w8(dt, x, wg8, wu8, wd8, sg, su, sd, ids, w, tokens=None, want_p
     rc = lib().oracle_moe_forward_w8(dt, _ptr(xs), *[_ptr(a) for a in args], _ptr(ids), _ptr(w),
                                      T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
     assert rc == 0, "oracle_moe_forward_w8 rejected its arguments"
+    return (y, hp, ep) if want_pairs else y
+
+
+def quantize_int8_rows(dt, a):
+    """oracle_quantize_int8_rows: per-row int8 codes in [-127, 127] and fp32
+    scales (amax / 127, 1 for a zero row). a: [..., cols] storage of dtype dt.
+    Returns (codes int8 of a's shape, scales float32 of a's shape[:-1])."""
+    s_ = _storage(np.asarray(a), dt)
+    cols = s_.shape[-1]
+    rows = s_.size // cols
+    q = np.empty(s_.shape, np.int8)
+    sc = np.empty(s_.shape[:-1], np.float32)
+    assert lib().oracle_quantize_int8_rows(dt, _ptr(s_), rows, cols, _ptr(q), _ptr(sc)) == 0
+    return q, sc
+
+
+def quantize_int4_rows(dt, w):
+    """oracle_quantize_int4_rows: per-row int4 codes in [-8, 7] (amax / 7
+    scales, 1 for a zero row), packed two per byte, element 2i in the low
+    nibble. w: [..., cols] (cols even). Returns (packed uint8 [..., cols/2],
+    scales float32 of w's shape[:-1])."""
+    ws = _storage(np.asarray(w), dt)
+    cols = ws.shape[-1]
+    rows = ws.size // cols
+    q = np.empty(ws.shape[:-1] + (cols // 2,), np.uint8)
+    sc = np.empty(ws.shape[:-1], np.float32)
+    assert lib().oracle_quantize_int4_rows(dt, _ptr(ws), rows, cols, _ptr(q), _ptr(sc)) == 0
+    return q, sc
+
+
+def w4a8_gemm(A, B):
+    """oracle_w4a8_gemm: Ct [N, M] int32 = sum_k A[m, k] * B4[n, k], A int8
+    [M, K], B packed int4 uint8 [N, K/2]."""
+    A = _c(A, np.int8)
+    B = _c(B, np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] * 2 == K
+    Ct = np.empty((N, M), np.int32)
+    rc = lib().oracle_w4a8_gemm(_ptr(A), _ptr(B), M, N, K, _ptr(Ct))
+    assert rc == 0, "oracle_w4a8_gemm: rejected arguments or int32 overflow (%d)" % rc
+    return Ct
+
+
+def moe_forward_w4a8(dt, x, wg4, wu4, wd4, sg, su, sd, ids, w, tokens=None, want_pairs=False):
+    """oracle_moe_forward_w4a8: the forward with int4 expert weights (packed
+    uint8 [E, D, H/2] / [E, D, H/2] / [E, H, D/2], fp32 row scales [E, D] /
+    [E, D] / [E, H]) and int8 activations. Same outputs as moe_forward."""
+    xs = _storage(x, dt)
+    T, H = xs.shape
+    E, D, _ = wg4.shape
+    K = ids.shape[1]
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tokens is None else len(tok)
+    y = np.empty((n, H), np.float32)
+    hp = np.empty((n * K, D), np.float32) if want_pairs else None
+    ep = np.empty((n * K, H), np.float32) if want_pairs else None
+    args = [_c(a, np.uint8) for a in (wg4, wu4, wd4)] + [_c(a, np.float32) for a in (sg, su, sd)]
+    rc = lib().oracle_moe_forward_w4a8(dt, _ptr(xs), *[_ptr(a) for a in args], _ptr(ids), _ptr(w),
+                                       T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
+    assert rc == 0, "oracle_moe_forward_w4a8 rejected its arguments"
     return (y, hp, ep) if want_pairs else y

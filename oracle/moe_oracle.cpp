@@ -433,6 +433,174 @@ int oracle_moe_forward_w8(int dt, const void* x, const uint8_t* wg8, const uint8
   return moe_forward(dt, x, W, ids, w, T, H, D, E, K, tokens, n_tokens, y, h_pairs, eo_pairs);
 }
 
+}  // extern "C"
+
+namespace {
+
+// ------------------------------------------------------------- W4A8 -------
+// Int4 weights with int8 activations ([B] w4a8_dequant_gemm: weights int4
+// packed two per uint8, activations int8, int32 accumulation; [B] module
+// docstring: the weight + activation mode, each side dequantised in the
+// kernel). Storage of a packed row: element 2i in bits 0..3 of byte i,
+// element 2i+1 in bits 4..7 ([B] the uint8 -> int4 unpack: the field at
+// position j % 2 is shifted right by 4 * (j % 2)); a field is a 4-bit two's
+// complement number in [-8, 7].
+int int4_at(const uint8_t* row, int64_t k) {
+  const int nib = (row[k >> 1] >> (4 * (k & 1))) & 0xF;
+  return nib >= 8 ? nib - 16 : nib;
+}
+
+// Symmetric per-row quantisation (the scheme is left open by the pages;
+// taken here): s = amax / qmax (1 for an all-zero row), q = the integer
+// nearest to v / s (fp32 division, ties to even), clamped to [qmin, qmax].
+template <typename Store>
+void quantize_rows(int dt, const void* v, int64_t rows, int cols, float qmax, float qmin,
+                   float* scales, Store store) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float amax = 0.0f;
+    for (int k = 0; k < cols; ++k) amax = std::fmax(amax, std::fabs(load_elem(dt, v, r * cols + k)));
+    const float s = amax > 0.0f ? amax / qmax : 1.0f;
+    scales[r] = s;
+    for (int k = 0; k < cols; ++k) {
+      float q = std::nearbyint(load_elem(dt, v, r * cols + k) / s);
+      q = std::fmin(std::fmax(q, qmin), qmax);
+      store(r, k, static_cast<int>(q));
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// int8 activations: qmax = 127, codes in [-127, 127].
+int oracle_quantize_int8_rows(int dt, const void* a, int64_t rows, int cols, int8_t* q,
+                              float* scales) {
+  if (!dtype_ok(dt) || rows < 0 || cols <= 0) return -1;
+  quantize_rows(dt, a, rows, cols, 127.0f, -127.0f, scales,
+                [&](int64_t r, int k, int v) { q[r * cols + k] = static_cast<int8_t>(v); });
+  return 0;
+}
+
+// int4 weights: qmax = 7, codes in [-8, 7], packed as above ([rows, cols/2]).
+int oracle_quantize_int4_rows(int dt, const void* w, int64_t rows, int cols, uint8_t* packed,
+                              float* scales) {
+  if (!dtype_ok(dt) || rows < 0 || cols <= 0 || cols % 2) return -1;
+  const int64_t half = cols / 2;
+  for (int64_t i = 0; i < rows * half; ++i) packed[i] = 0;
+  quantize_rows(dt, w, rows, cols, 7.0f, -8.0f, scales, [&](int64_t r, int k, int v) {
+    uint8_t& b = packed[r * half + k / 2];
+    b = static_cast<uint8_t>(b | ((v & 0xF) << (4 * (k % 2))));
+  });
+  return 0;
+}
+
+// [B] w4a8_dequant_gemm: Ct[n, m] = sum_k A[m, k] * B4[n, k] with A int8
+// [M, K], B packed int4 [N, K/2] and the int32 result written transposed,
+// [N, M]. Summed exactly (int64 here); returns -2 if a result leaves the
+// int32 range, which int32 accumulation could not represent.
+int oracle_w4a8_gemm(const int8_t* A, const uint8_t* B, int M, int N, int K, int32_t* Ct) {
+  if (M < 0 || N < 0 || K <= 0 || K % 2) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int n = 0; n < N; ++n) {
+    const uint8_t* brow = B + static_cast<int64_t>(n) * (K / 2);
+    for (int m = 0; m < M; ++m) {
+      int64_t acc = 0;
+      for (int k = 0; k < K; ++k) acc += static_cast<int64_t>(A[static_cast<int64_t>(m) * K + k]) * int4_at(brow, k);
+      if (acc > INT32_MAX || acc < INT32_MIN) bad = 1;
+      Ct[static_cast<int64_t>(n) * M + m] = static_cast<int32_t>(acc);
+    }
+  }
+  return bad ? -2 : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Dequantised dot product: (float) acc * s_a * s_w, left to right in fp32.
+float dequant(int64_t acc, float sa, float sw) { return static_cast<float>(acc) * sa * sw; }
+
+}  // namespace
+
+extern "C" {
+
+// The forward with W4A8 experts: x [T, H] (dtype dt) quantised per token to
+// int8 (oracle_quantize_int8_rows); per routed pair (token t, expert e):
+//   g_j  = dequant(sum_h xq[t,h] Wg4[e,j,h], sx[t], sg[e,j]),  u_j likewise
+//   h_j  = R(SiLU(g_j) * u_j)                     (dtype dt, as the 16-bit path)
+//   hq   = int8 quantisation of the pair's h row, scale sh
+//   eo_c = R(dequant(sum_j hq[j] Wd4[e,c,j], sh, sd[e,c]))
+// then y[t] = the fp32 fma sum over k ascending of w[t,k] * eo (masked slots
+// skipped), as oracle_moe_forward. Weights: packed int4 [E, D, H/2] (gate,
+// up) and [E, H, D/2] (down) with fp32 row scales [E*D] / [E*H].
+int oracle_moe_forward_w4a8(int dt, const void* x, const uint8_t* wg4, const uint8_t* wu4,
+                            const uint8_t* wd4, const float* sg, const float* su, const float* sd,
+                            const int32_t* ids, const float* w, int T, int H, int D, int E, int K,
+                            const int32_t* tokens, int n_tokens, float* y, float* h_pairs,
+                            float* eo_pairs) {
+  if (!dtype_ok(dt) || T < 0 || H <= 0 || D <= 0 || E <= 0 || K <= 0 || H % 2 || D % 2) return -1;
+  if (!tokens && n_tokens != T) return -1;
+  for (int i = 0; i < n_tokens; ++i) {
+    const int t = tokens ? tokens[i] : i;
+    if (t < 0 || t >= T) return -1;
+    for (int k = 0; k < K; ++k) {
+      if (ids[static_cast<int64_t>(t) * K + k] >= E) return -1;
+    }
+  }
+#pragma omp parallel
+  {
+    std::vector<int8_t> xq(H), hq(D);
+    std::vector<float> hbuf(D), eo(H), acc(H);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < n_tokens; ++i) {
+      const int t = tokens ? tokens[i] : i;
+      float sx = 0.0f;
+      quantize_rows(dt, static_cast<const char*>(x) + static_cast<int64_t>(t) * H * (dt == kF32 ? 4 : 2),
+                    1, H, 127.0f, -127.0f, &sx, [&](int64_t, int k, int v) { xq[k] = static_cast<int8_t>(v); });
+      for (int c = 0; c < H; ++c) acc[c] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int64_t slot = static_cast<int64_t>(t) * K + k;
+        const int64_t out_slot = static_cast<int64_t>(i) * K + k;
+        const int e = ids[slot];
+        if (e < 0) {
+          if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = 0.0f;
+          if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = 0.0f;
+          continue;
+        }
+        for (int j = 0; j < D; ++j) {
+          const int64_t row = static_cast<int64_t>(e) * D + j;
+          int64_t ag = 0, au = 0;
+          for (int c = 0; c < H; ++c) {
+            ag += static_cast<int64_t>(xq[c]) * int4_at(wg4 + row * (H / 2), c);
+            au += static_cast<int64_t>(xq[c]) * int4_at(wu4 + row * (H / 2), c);
+          }
+          const float g = dequant(ag, sx, sg[row]);
+          const float u = dequant(au, sx, su[row]);
+          hbuf[j] = round_to(dt, silu(g) * u);
+        }
+        float sh = 0.0f;
+        quantize_rows(kF32, hbuf.data(), 1, D, 127.0f, -127.0f, &sh,
+                      [&](int64_t, int j, int v) { hq[j] = static_cast<int8_t>(v); });
+        for (int c = 0; c < H; ++c) {
+          const int64_t row = static_cast<int64_t>(e) * H + c;
+          int64_t ad = 0;
+          for (int j = 0; j < D; ++j) ad += static_cast<int64_t>(hq[j]) * int4_at(wd4 + row * (D / 2), j);
+          eo[c] = round_to(dt, dequant(ad, sh, sd[row]));
+        }
+        const float wk = w[slot];
+        for (int c = 0; c < H; ++c) acc[c] = std::fma(wk, eo[c], acc[c]);
+        if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = hbuf[j];
+        if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = eo[c];
+      }
+      for (int c = 0; c < H; ++c) y[static_cast<int64_t>(i) * H + c] = acc[c];
+    }
+  }
+  return 0;
+}
+
 // -------------------------------------------------------- weighted reduce --
 // moe_reduce_fused ([C] sections 1-2) and its scaled variants ([C] section 1
 // and the commit note on the scaled variants: with_x_sf multiplies once per
