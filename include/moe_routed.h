@@ -252,6 +252,67 @@ moe_status moe_routed_forward_w8(const void* x, const uint8_t* w_gate, const uin
                                  int dtype, void* workspace, size_t workspace_bytes, void* y,
                                  void* stream);
 
+/* W4A8 experts ([B] w4a8_dequant_gemm and the module docstring's weight +
+ * activation mode: int4 weights packed two per uint8, int8 activations,
+ * int32 accumulation; the quantisation scheme is left open by the pages and
+ * taken here as symmetric per row).
+ * Packed int4 rows: field 2i in bits 0..3 of byte i, field 2i+1 in bits
+ * 4..7, each a 4-bit two's complement number in [-8, 7].
+ *
+ * moe_quantize_int8_rows: per row r of `rows` rows of `cols` values of dtype
+ * (MOE_F16, MOE_BF16, MOE_F32): scales[r] = max_k |a[r,k]| / 127 (1 for an
+ * all-zero row), q[r,k] = clamp(nearest integer to a[r,k] / scales[r] (fp32
+ * division, ties to even), -127, 127). q int8 [rows, cols], scales fp32 [rows].
+ *
+ * moe_quantize_int4_rows: the same with 7 in place of 127 and codes clamped
+ * to [-8, 7], packed: packed uint8 [rows, cols / 2] (cols even).
+ * Both: errors MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP. */
+moe_status moe_quantize_int8_rows(const void* a, int64_t rows, int cols, int dtype, int8_t* q,
+                                  float* scales, void* stream);
+moe_status moe_quantize_int4_rows(const void* w, int64_t rows, int cols, int dtype,
+                                  uint8_t* packed, float* scales, void* stream);
+
+/* The plain W4A8 GEMM of [B] w4a8_dequant_gemm:
+ *   Ct[n, m] = sum_k A[m, k] * B4[n, k]   (exact, int32)
+ *   A  int8 [M, K];  B  packed int4 uint8 [N, K/2];  Ct  int32 [N, M]
+ *   (written transposed, as in [B]).
+ * Requires M >= 1, N % 256 == 0, K % 256 == 0 and K <= 131072 (the kernel
+ * accumulates 16 x the products in int32). Ct is overwritten. Errors:
+ * MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_HIP. */
+moe_status moe_w4a8_gemm(const int8_t* A, const uint8_t* B, int M, int N, int K, int32_t* Ct,
+                         void* stream);
+
+/* moe_expert_gate_up / moe_expert_down with W4A8 experts: w_gate, w_up
+ * packed int4 [E, D, H/2] and w_down [E, H, D/2] with fp32 row scales
+ * s_gate, s_up [E, D], s_down [E, H]; activations int8 with one fp32 scale
+ * per row: xq [T, H] with sx [T] (token order; gathered through
+ * sorted_token), hq [P, D] with sh [P] (sorted order). With
+ * dq(acc, sa, sw) = (float) acc * sa * sw (fp32, left to right):
+ *   g = dq(xq[t] . Wg4[e,j], sx[t], s_gate[e,j]),  u likewise,
+ *   h[i, j] = R(SiLU(g) * u),
+ *   expert_out[i, c] = R(dq(hq[i] . Wd4[e,c], sh[i], s_down[e,c])),
+ * dot products exact in int32. dtype (of h / expert_out): MOE_F16 or
+ * MOE_BF16. Requires D % 256 == 0 besides the 16-bit calls' rules.
+ *
+ * moe_routed_forward_w4a8 runs: x -> xq, sx (moe_quantize_int8_rows);
+ * gate/up -> h; h -> hq, sh (per sorted row); down -> expert_out;
+ * moe_reduce_fused -> y. Its workspace (moe_forward_w4a8_workspace_bytes,
+ * 256-byte aligned) holds h, expert_out (as moe_routed_forward's) and then
+ * xq, sx, hq, sh. Errors as the 16-bit calls. */
+moe_status moe_expert_gate_up_w4a8(const int8_t* xq, const float* sx, const uint8_t* w_gate,
+                                   const uint8_t* w_up, const float* s_gate, const float* s_up,
+                                   const moe_tables* tables, int H, int D, int dtype, void* h,
+                                   void* stream);
+moe_status moe_expert_down_w4a8(const int8_t* hq, const float* sh, const uint8_t* w_down,
+                                const float* s_down, const moe_tables* tables, int H, int D,
+                                int dtype, void* expert_out, void* stream);
+size_t moe_forward_w4a8_workspace_bytes(int T, int K, int H, int D, int dtype);
+moe_status moe_routed_forward_w4a8(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                   const uint8_t* w_down, const float* s_gate, const float* s_up,
+                                   const float* s_down, const moe_tables* tables, int H, int D,
+                                   int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                   void* stream);
+
 /* Step 3: top-k weighted reduce back to token order ([C] sections 1-2):
  *   y[t, :] = R_out( sum over k = 0..K-1 ascending with pos[t,k] >= 0 of
  *                    w[t,k] * expert_out[pos[t,k], :] )

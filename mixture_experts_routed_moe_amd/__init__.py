@@ -23,7 +23,10 @@ from ._lib import (MOE_BF16, MOE_ERR_DTYPE, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_F16
 __all__ = ["MoeError", "MoeTables", "FP8Weights", "default_block_m", "moe_gate", "moe_dispatch",
            "quantize_fp8_rows", "moe_expert_gate_up_w8", "moe_expert_down_w8",
            "moe_routed_forward_w8", "moe_expert_gate_up",
-           "moe_expert_down", "moe_routed_forward", "moe_reduce_fused", "forward_workspace"]
+           "moe_expert_down", "moe_routed_forward", "moe_reduce_fused", "forward_workspace",
+           "W4Weights", "quantize_int8_rows", "quantize_int4_rows", "w4a8_gemm",
+           "moe_expert_gate_up_w4a8", "moe_expert_down_w4a8", "forward_w4a8_workspace",
+           "moe_routed_forward_w4a8"]
 
 _DTYPE_CODE = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
 # The reduce also reads and writes OCP FP8 E4M3 ("fn").
@@ -337,6 +340,178 @@ def moe_routed_forward_w8(x, w_gate, w_up, w_down, tables, y=None, workspace=Non
                                       _ptr(w_up.scales), _ptr(w_down.scales), tables.ref, H, D,
                                       _DTYPE_CODE[x.dtype], _ptr(workspace), workspace.numel(),
                                       _ptr(y), _stream(x.device)))
+    return y
+
+
+class W4Weights:
+    """Stacked expert weights in int4: `packed` uint8 [E, N, Kd/2] (field 2i
+    in the low nibble of byte i) and one fp32 scale per row, `scales` [E, N]
+    (value = scale * field). `shape` is the logical [E, N, Kd]."""
+
+    def __init__(self, packed, scales):
+        _check_tensor(packed, "packed", torch.uint8, 3)
+        _check_tensor(scales, "scales", torch.float32, 2, packed.device)
+        _require(tuple(scales.shape) == tuple(packed.shape[:2]), MOE_ERR_SHAPE,
+                 "scales must be [E, N] = %s" % (tuple(packed.shape[:2]),))
+        self.packed = packed
+        self.scales = scales
+
+    @property
+    def shape(self):
+        E, N, half = self.packed.shape
+        return torch.Size((E, N, 2 * half))
+
+    def dim(self):
+        return 3
+
+
+def quantize_int8_rows(a):
+    """moe_quantize_int8_rows on a [rows, cols] (fp16 / bf16 / fp32): int8
+    codes in [-127, 127] and fp32 scales amax / 127. Returns (q, scales)."""
+    _check_tensor(a, "a", None, 2)
+    _require(a.dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "a must be float16, bfloat16 or float32")
+    rows, cols = a.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=a.device)
+    scales = torch.empty((rows,), dtype=torch.float32, device=a.device)
+    check(lib().moe_quantize_int8_rows(_ptr(a), rows, cols, _DTYPE_CODE[a.dtype], _ptr(q),
+                                       _ptr(scales), _stream(a.device)))
+    return q, scales
+
+
+def quantize_int4_rows(w):
+    """moe_quantize_int4_rows on stacked weights w [E, N, Kd] (Kd even):
+    per-row scale amax / 7 and int4 codes in [-8, 7], packed. Returns
+    W4Weights."""
+    _check_tensor(w, "w", None, 3)
+    _require(w.dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "w must be float16, bfloat16 or float32")
+    E, N, Kd = w.shape
+    _require(Kd % 2 == 0, MOE_ERR_SHAPE, "the row length must be even")
+    packed = torch.empty((E, N, Kd // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, N), dtype=torch.float32, device=w.device)
+    check(lib().moe_quantize_int4_rows(_ptr(w), E * N, Kd, _DTYPE_CODE[w.dtype], _ptr(packed),
+                                       _ptr(scales), _stream(w.device)))
+    return W4Weights(packed, scales)
+
+
+def w4a8_gemm(A, B, Ct=None):
+    """moe_w4a8_gemm: Ct [N, M] int32 = sum_k A[m, k] * B4[n, k] for A int8
+    [M, K] and packed int4 B uint8 [N, K/2]."""
+    _check_tensor(A, "A", torch.int8, 2)
+    _check_tensor(B, "B", torch.uint8, 2, A.device)
+    M, K = A.shape
+    N = B.shape[0]
+    _require(B.shape[1] * 2 == K, MOE_ERR_SHAPE, "B must be [N, K/2] (got %s)" % (tuple(B.shape),))
+    if Ct is None:
+        Ct = torch.empty((N, M), dtype=torch.int32, device=A.device)
+    _check_tensor(Ct, "Ct", torch.int32, 2, A.device)
+    _require(tuple(Ct.shape) == (N, M), MOE_ERR_SHAPE, "Ct must be [N, M]")
+    check(lib().moe_w4a8_gemm(_ptr(A), _ptr(B), M, N, K, _ptr(Ct), _stream(A.device)))
+    return Ct
+
+
+def _w4_shapes(act, scales, w_a, w_b, w_down, tables, gate_up, dtype):
+    _require(dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "W4A8 experts produce float16 or bfloat16")
+    _check_tensor(act, "activations", torch.int8, 2, tables.device)
+    _check_tensor(scales, "activation scales", torch.float32, 1, tables.device)
+    for n, w in (("w_a", w_a), ("w_b", w_b), ("w_down", w_down)):
+        if w is not None:
+            _require(isinstance(w, W4Weights), MOE_ERR_DTYPE, "%s must be W4Weights" % n)
+            _require(w.packed.device == tables.device, MOE_ERR_SHAPE, "%s is on another device" % n)
+    E = tables.E
+    rows, kd = act.shape
+    _require(scales.shape[0] == rows, MOE_ERR_SHAPE, "one activation scale per row")
+    if gate_up:
+        _require(rows == tables.T, MOE_ERR_SHAPE, "xq has %d rows, tables %d tokens" % (rows, tables.T))
+        H = kd
+        _require(w_a.shape[0] == E and w_a.shape[2] == H, MOE_ERR_SHAPE,
+                 "w_gate must be [E=%d, D, H=%d] (got %s)" % (E, H, tuple(w_a.shape)))
+        D = w_a.shape[1]
+        _require(tuple(w_b.shape) == (E, D, H), MOE_ERR_SHAPE, "w_up must be [%d, %d, %d]" % (E, D, H))
+        if w_down is not None:
+            _require(tuple(w_down.shape) == (E, H, D), MOE_ERR_SHAPE,
+                     "w_down must be [%d, %d, %d]" % (E, H, D))
+        return H, D
+    _require(rows == tables.T * tables.K, MOE_ERR_SHAPE, "hq must have T*K rows")
+    D = kd
+    _require(w_a.shape[0] == E and w_a.shape[2] == D, MOE_ERR_SHAPE,
+             "w_down must be [E=%d, H, D=%d] (got %s)" % (E, D, tuple(w_a.shape)))
+    return w_a.shape[1], D
+
+
+def moe_expert_gate_up_w4a8(xq, sx, w_gate, w_up, tables, dtype=torch.bfloat16, h=None):
+    """Step 2a with W4A8 experts: xq int8 [T, H] with scales sx [T] against
+    W4Weights [E, D, H]; h [T*K, D] of dtype."""
+    H, D = _w4_shapes(xq, sx, w_gate, w_up, None, tables, True, dtype)
+    if h is None:
+        h = torch.empty(tables.T * tables.K, D, dtype=dtype, device=xq.device)
+    _check_tensor(h, "h", dtype, 2, tables.device)
+    check(lib().moe_expert_gate_up_w4a8(_ptr(xq), _ptr(sx), _ptr(w_gate.packed), _ptr(w_up.packed),
+                                        _ptr(w_gate.scales), _ptr(w_up.scales), tables.ref, H, D,
+                                        _DTYPE_CODE[dtype], _ptr(h), _stream(xq.device)))
+    return h
+
+
+def moe_expert_down_w4a8(hq, sh, w_down, tables, dtype=torch.bfloat16, expert_out=None):
+    """Step 2b with W4A8 experts: hq int8 [T*K, D] with scales sh [T*K]
+    against W4Weights [E, H, D]; expert_out [T*K, H] of dtype."""
+    H, D = _w4_shapes(hq, sh, w_down, None, None, tables, False, dtype)
+    if expert_out is None:
+        expert_out = torch.empty(tables.T * tables.K, H, dtype=dtype, device=hq.device)
+    _check_tensor(expert_out, "expert_out", dtype, 2, tables.device)
+    check(lib().moe_expert_down_w4a8(_ptr(hq), _ptr(sh), _ptr(w_down.packed), _ptr(w_down.scales),
+                                     tables.ref, H, D, _DTYPE_CODE[dtype], _ptr(expert_out),
+                                     _stream(hq.device)))
+    return expert_out
+
+
+def forward_w4a8_workspace(tables, H, D, dtype):
+    """A workspace for moe_routed_forward_w4a8 and views of its buffers:
+    (ws, h, expert_out, xq, sx, hq, sh)."""
+    code = _DTYPE_CODE[dtype]
+    nbytes = lib().moe_forward_w4a8_workspace_bytes(tables.T, tables.K, H, D, code)
+    _require(nbytes > 0, MOE_ERR_SHAPE, "invalid workspace sizes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=tables.device)
+    base = lib().moe_forward_workspace_bytes(tables.T, tables.K, H, D, code)
+    off = lib().moe_forward_workspace_expert_out_offset(tables.T, tables.K, H, D, code)
+    T, P = tables.T, tables.T * tables.K
+    esz = torch.empty((), dtype=dtype).element_size()
+    up = lambda v: (v + 255) // 256 * 256
+    h = ws[:P * D * esz].view(dtype).view(P, D)
+    eo = ws[off:off + P * H * esz].view(dtype).view(P, H)
+    o_xq = base
+    o_sx = o_xq + up(T * H)
+    o_hq = o_sx + up(T * 4)
+    o_sh = o_hq + up(P * D)
+    xq = ws[o_xq:o_xq + T * H].view(torch.int8).view(T, H)
+    sx = ws[o_sx:o_sx + T * 4].view(torch.float32)
+    hq = ws[o_hq:o_hq + P * D].view(torch.int8).view(P, D)
+    sh = ws[o_sh:o_sh + P * 4].view(torch.float32)
+    return ws, h, eo, xq, sx, hq, sh
+
+
+def moe_routed_forward_w4a8(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
+    """Steps 2-3 with W4A8 experts (W4Weights; x 16-bit, quantised to int8
+    per token inside): y [T, H] of x.dtype."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    _require(x.dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "W4A8 experts take float16 or bfloat16 activations")
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _require(isinstance(w, W4Weights), MOE_ERR_DTYPE, "%s must be W4Weights" % n)
+        _require(w.packed.device == tables.device, MOE_ERR_SHAPE, "%s is on another device" % n)
+    H, D = _expert_shapes(x, w_gate, w_up, w_down, tables, True)
+    if workspace is None:
+        workspace = forward_w4a8_workspace(tables, H, D, x.dtype)[0]
+    _check_tensor(workspace, "workspace", torch.uint8, 1, tables.device)
+    if y is None:
+        y = torch.empty(tables.T, H, dtype=x.dtype, device=x.device)
+    _check_tensor(y, "y", x.dtype, 2, tables.device)
+    _require(tuple(y.shape) == (tables.T, H), MOE_ERR_SHAPE, "y must be [T, H]")
+    check(lib().moe_routed_forward_w4a8(_ptr(x), _ptr(w_gate.packed), _ptr(w_up.packed),
+                                        _ptr(w_down.packed), _ptr(w_gate.scales),
+                                        _ptr(w_up.scales), _ptr(w_down.scales), tables.ref, H, D,
+                                        _DTYPE_CODE[x.dtype], _ptr(workspace), workspace.numel(),
+                                        _ptr(y), _stream(x.device)))
     return y
 
 

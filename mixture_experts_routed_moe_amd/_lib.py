@@ -87,6 +87,21 @@ def lib():
         L.moe_reduce_fused_scaled.argtypes = [vp, i64, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                               vp, vp]
         L.moe_reduce_fused_scaled.restype = i32
+        L.moe_quantize_int8_rows.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.moe_quantize_int8_rows.restype = i32
+        L.moe_quantize_int4_rows.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.moe_quantize_int4_rows.restype = i32
+        L.moe_w4a8_gemm.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+        L.moe_w4a8_gemm.restype = i32
+        L.moe_expert_gate_up_w4a8.argtypes = [vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_gate_up_w4a8.restype = i32
+        L.moe_expert_down_w4a8.argtypes = [vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_down_w4a8.restype = i32
+        L.moe_forward_w4a8_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_forward_w4a8_workspace_bytes.restype = sz
+        L.moe_routed_forward_w4a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp,
+                                              sz, vp, vp]
+        L.moe_routed_forward_w4a8.restype = i32
         _lib = L
     return _lib
 

@@ -122,6 +122,36 @@ moe_status check_expert_shapes(const moe_tables* t, int H, int D, int dtype) {
   return MOE_OK;
 }
 
+// W4A8 reductions: 16 x the dot product must fit in int32 (|a| <= 128,
+// |16 q| <= 128 per term).
+constexpr int kW4MaxK = 131072;
+
+moe_status check_w4a8_shapes(const moe_tables* t, int H, int D, int dtype) {
+  moe_status s = check_expert_shapes(t, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (!is_16bit(dtype)) return fail(MOE_ERR_DTYPE, "W4A8 experts take MOE_F16 or MOE_BF16 activations");
+  if (D % 256 != 0) return fail(MOE_ERR_SHAPE, "W4A8 experts need D a multiple of 256 (got %d)", D);
+  if (H > kW4MaxK || D > kW4MaxK) return fail(MOE_ERR_SHAPE, "W4A8 reductions are limited to %d", kW4MaxK);
+  return MOE_OK;
+}
+
+// Workspace of the W4A8 forward: the 16-bit forward's h and expert_out, then
+// xq [T, H] int8, sx [T], hq [P, D] int8, sh [P] (fp32), each 256-aligned.
+struct W4Layout {
+  size_t xq, sx, hq, sh, total;
+};
+
+W4Layout w4_layout(int T, int K, int H, int D, size_t base) {
+  const size_t P = static_cast<size_t>(T) * K;
+  W4Layout L;
+  L.xq = base;
+  L.sx = L.xq + align_up(static_cast<size_t>(T) * H);
+  L.hq = L.sx + align_up(static_cast<size_t>(T) * 4);
+  L.sh = L.hq + align_up(P * D);
+  L.total = L.sh + align_up(P * 4);
+  return L;
+}
+
 size_t ws_h_bytes(int T, int K, int D, int dtype) {
   return static_cast<size_t>(T) * K * D * dtype_bytes(dtype);
 }
@@ -356,6 +386,123 @@ moe_status moe_routed_forward_w8(const void* x, const uint8_t* w_gate, const uin
   err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
                            nullptr, tables->T, tables->K, H, dtype, dtype, y, st);
   return hip_status(err, "moe_routed_forward_w8 reduce launch");
+}
+
+moe_status moe_quantize_int8_rows(const void* a, int64_t rows, int cols, int dtype, int8_t* q,
+                                  float* scales, void* stream) {
+  if (!a || !q || !scales) return fail(MOE_ERR_NULL, "a, q and scales must not be NULL");
+  if (rows < 0 || cols <= 0) return fail(MOE_ERR_SHAPE, "rows must be >= 0 and cols > 0");
+  if (rows > (int64_t{1} << 33)) return fail(MOE_ERR_SHAPE, "too many rows for one launch");
+  if (!is_float(dtype)) return fail(MOE_ERR_DTYPE, "dtype must be MOE_F16, MOE_BF16 or MOE_F32");
+  if (rows == 0) return ok();
+  return hip_status(moe::launch_quantize_int8_rows(a, rows, cols, dtype, q, scales,
+                                                   static_cast<hipStream_t>(stream)),
+                    "moe_quantize_int8_rows launch");
+}
+
+moe_status moe_quantize_int4_rows(const void* w, int64_t rows, int cols, int dtype,
+                                  uint8_t* packed, float* scales, void* stream) {
+  if (!w || !packed || !scales) return fail(MOE_ERR_NULL, "w, packed and scales must not be NULL");
+  if (rows < 0 || cols <= 0 || cols % 2 != 0) {
+    return fail(MOE_ERR_SHAPE, "rows must be >= 0 and cols a positive even number");
+  }
+  if (rows > (int64_t{1} << 33)) return fail(MOE_ERR_SHAPE, "too many rows for one launch");
+  if (!is_float(dtype)) return fail(MOE_ERR_DTYPE, "dtype must be MOE_F16, MOE_BF16 or MOE_F32");
+  if (rows == 0) return ok();
+  return hip_status(moe::launch_quantize_int4_rows(w, rows, cols, dtype, packed, scales,
+                                                   static_cast<hipStream_t>(stream)),
+                    "moe_quantize_int4_rows launch");
+}
+
+moe_status moe_w4a8_gemm(const int8_t* A, const uint8_t* B, int M, int N, int K, int32_t* Ct,
+                         void* stream) {
+  if (!A || !B || !Ct) return fail(MOE_ERR_NULL, "A, B and Ct must not be NULL");
+  if (M < 1) return fail(MOE_ERR_SHAPE, "M must be >= 1 (got %d)", M);
+  if (N <= 0 || N % 256 != 0) return fail(MOE_ERR_SHAPE, "N must be a positive multiple of 256 (got %d)", N);
+  if (K <= 0 || K % 256 != 0 || K > kW4MaxK) {
+    return fail(MOE_ERR_SHAPE, "K must be a positive multiple of 256, at most %d (got %d)", kW4MaxK, K);
+  }
+  if (static_cast<int64_t>(N) * M >= (int64_t{1} << 31)) return fail(MOE_ERR_SHAPE, "N * M too large");
+  return hip_status(moe::launch_w4a8_gemm(A, B, M, N, K, Ct, static_cast<hipStream_t>(stream)),
+                    "moe_w4a8_gemm launch");
+}
+
+moe_status moe_expert_gate_up_w4a8(const int8_t* xq, const float* sx, const uint8_t* w_gate,
+                                   const uint8_t* w_up, const float* s_gate, const float* s_up,
+                                   const moe_tables* tables, int H, int D, int dtype, void* h,
+                                   void* stream) {
+  if (!xq || !sx || !w_gate || !w_up || !s_gate || !s_up || !h) {
+    return fail(MOE_ERR_NULL, "xq, sx, w_gate, w_up, s_gate, s_up and h must not be NULL");
+  }
+  moe_status s = check_w4a8_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  moe::W4GemmProblem p{xq, sx, w_gate, w_up, s_gate, s_up, h, D, H, dtype};
+  return hip_status(moe::launch_gate_up_w4a8(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_gate_up_w4a8 launch");
+}
+
+moe_status moe_expert_down_w4a8(const int8_t* hq, const float* sh, const uint8_t* w_down,
+                                const float* s_down, const moe_tables* tables, int H, int D,
+                                int dtype, void* expert_out, void* stream) {
+  if (!hq || !sh || !w_down || !s_down || !expert_out) {
+    return fail(MOE_ERR_NULL, "hq, sh, w_down, s_down and expert_out must not be NULL");
+  }
+  moe_status s = check_w4a8_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  moe::W4GemmProblem p{hq, sh, w_down, nullptr, s_down, nullptr, expert_out, H, D, dtype};
+  return hip_status(moe::launch_down_w4a8(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_down_w4a8 launch");
+}
+
+size_t moe_forward_w4a8_workspace_bytes(int T, int K, int H, int D, int dtype) {
+  const size_t base = moe_forward_workspace_bytes(T, K, H, D, dtype);
+  if (base == 0) return 0;
+  const W4Layout L = w4_layout(T, K, H, D, base);
+  return L.total;
+}
+
+moe_status moe_routed_forward_w4a8(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                   const uint8_t* w_down, const float* s_gate, const float* s_up,
+                                   const float* s_down, const moe_tables* tables, int H, int D,
+                                   int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                   void* stream) {
+  if (!x || !w_gate || !w_up || !w_down || !s_gate || !s_up || !s_down || !workspace || !y) {
+    return fail(MOE_ERR_NULL,
+                "x, the weights, their scales, workspace and y must not be NULL");
+  }
+  moe_status s = check_w4a8_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  const size_t need = moe_forward_w4a8_workspace_bytes(tables->T, tables->K, H, D, dtype);
+  if (workspace_bytes < need) {
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) {
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const int T = tables->T, K = tables->K;
+  const int64_t P = static_cast<int64_t>(T) * K;
+  char* ws = static_cast<char*>(workspace);
+  const W4Layout L = w4_layout(T, K, H, D, moe_forward_workspace_bytes(T, K, H, D, dtype));
+  void* hbuf = ws;
+  void* eo = ws + moe_forward_workspace_expert_out_offset(T, K, H, D, dtype);
+  int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+  float* sx = reinterpret_cast<float*>(ws + L.sx);
+  int8_t* hq = reinterpret_cast<int8_t*>(ws + L.hq);
+  float* sh = reinterpret_cast<float*>(ws + L.sh);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = moe::launch_quantize_int8_rows(x, T, H, dtype, xq, sx, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w4a8 x quantisation launch");
+  moe::W4GemmProblem up{xq, sx, w_gate, w_up, s_gate, s_up, hbuf, D, H, dtype};
+  err = moe::launch_gate_up_w4a8(up, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w4a8 gate/up launch");
+  err = moe::launch_quantize_int8_rows(hbuf, P, D, dtype, hq, sh, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w4a8 h quantisation launch");
+  moe::W4GemmProblem down{hq, sh, w_down, nullptr, s_down, nullptr, eo, H, D, dtype};
+  err = moe::launch_down_w4a8(down, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w4a8 down launch");
+  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
+                           nullptr, T, K, H, dtype, dtype, y, st);
+  return hip_status(err, "moe_routed_forward_w4a8 reduce launch");
 }
 
 moe_status moe_reduce_fused_scaled(const void* expert_out, int64_t rows,

@@ -32,6 +32,28 @@ hipError_t launch_gate_up_w8(const GemmProblem& p, const moe_tables& t, hipStrea
 hipError_t launch_down_w8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_quantize_fp8_rows(const void* w, int64_t rows, int cols, int dtype, uint8_t* q,
                                     float* scales, hipStream_t stream);
+// W4A8: int8 activations (per-row scales sa) against packed int4 weights
+// (b0 / b1, per-row scales s0 / s1); output c in dtype (kF16 / kBF16).
+struct W4GemmProblem {
+  const int8_t* a;       // gate/up: xq [T, kd]; down: hq [P, kd]
+  const float* sa;       // gate/up: sx [T] (by token); down: sh [P] (by row)
+  const uint8_t* b0;     // gate/up: W_gate [E, n, kd/2]; down: W_down
+  const uint8_t* b1;     // gate/up: W_up; down: unused
+  const float* s0;
+  const float* s1;
+  void* c;               // gate/up: h [P, n]; down: expert_out [P, n]
+  int n;
+  int kd;
+  int dtype;
+};
+hipError_t launch_gate_up_w4a8(const W4GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_down_w4a8(const W4GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_w4a8_gemm(const int8_t* A, const uint8_t* B, int M, int N, int K, int32_t* Ct,
+                            hipStream_t stream);
+hipError_t launch_quantize_int8_rows(const void* a, int64_t rows, int cols, int dtype, int8_t* q,
+                                     float* scales, hipStream_t stream);
+hipError_t launch_quantize_int4_rows(const void* w, int64_t rows, int cols, int dtype,
+                                     uint8_t* packed, float* scales, hipStream_t stream);
 hipError_t launch_gate_up_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 

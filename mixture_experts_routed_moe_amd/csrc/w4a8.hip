@@ -1,0 +1,503 @@
+// W4A8: int4 weights (packed two per byte) with int8 activations and int32
+// accumulation, on v_mfma_i32_32x32x32_i8 (TileLang tutorial ch.18,
+// w4a8_dequant_gemm: the packed weights are unpacked in registers and fed to
+// the integer GEMM; module docstring: the weight + activation quantised mode).
+//
+// Formats. A packed row holds field 2i in bits 0..3 of byte i and field 2i+1
+// in bits 4..7; a field is a 4-bit two's complement number in [-8, 7].
+// Quantisation is symmetric per row (the scheme is left open by the pages):
+// int8 activations s = amax / 127, int4 weights s = amax / 7 (1 for a zero
+// row), code = the nearest integer to v / s (fp32 division, ties to even),
+// clamped to [-127, 127] / [-8, 7].
+//
+// Unpacking. A packed word holds 8 fields; (w << 4) & 0xF0F0F0F0 puts fields
+// 0, 2, 4, 6 and w & 0xF0F0F0F0 fields 1, 3, 5, 7 at the top of a byte each,
+// which as an int8 is 16 x the field (sign included), and one byte permute
+// per 4 fields restores field order. The MFMA then accumulates 16 x the dot
+// product; an arithmetic shift by 4 returns it exactly as long as 16 x the
+// sum fits in int32 (|a| <= 128, |16 q| <= 128: K <= 131072).
+//
+// Tiling (both kernels): 256 threads = 4 waves; the reduction runs in
+// chunks of 256 elements, in which lane half h of a lane owns elements
+// 128h..128h+127 of its weight rows: 64 contiguous bytes per row and chunk
+// (two lanes per 128-byte segment), four 16-byte loads. k-slice t (0..7) of
+// the chunk is elements 128h + 16t .. +15 on both operands. The activation
+// rows of a chunk (32 rows x 256 bytes) are staged through a double-buffered
+// LDS tile; the weights stream straight from HBM into registers with a
+// 4-deep ring, as in the 16-bit grouped GEMM.
+
+#include <type_traits>
+#include <utility>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kCK = 256;                 // reduction elements per chunk
+constexpr int kLdsRow = kCK + 16;        // bytes per LDS A row (16 bytes of padding)
+constexpr int kStages = 4;               // weight chunks in the register ring
+
+__device__ __forceinline__ i32x16 mfma_i8(u32x4 a, u32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// 8 packed int4 fields -> 8 int8 bytes holding 16 x each field, in order.
+__device__ __forceinline__ u32x2 unpack8(uint32_t w) {
+  const uint32_t lo = (w << 4) & 0xF0F0F0F0u;   // fields 0, 2, 4, 6
+  const uint32_t hi = w & 0xF0F0F0F0u;          // fields 1, 3, 5, 7
+  // v_perm_b32: selector bytes 0..3 pick bytes of the second operand, 4..7
+  // bytes of the first.
+  return u32x2{__builtin_amdgcn_perm(hi, lo, 0x05010400u),
+               __builtin_amdgcn_perm(hi, lo, 0x07030602u)};
+}
+
+// A lane's weights of one chunk: two rows x 64 bytes (128 fields each).
+struct W4Chunk {
+  u32x4 v[2][4];
+
+  __device__ __forceinline__ void load(const uint8_t* const* p, int64_t byte_off) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[j][i] = *reinterpret_cast<const u32x4*>(p[j] + byte_off + i * 16);
+    }
+  }
+
+  // MFMA operand of row j for k-slice t: fields 16t..16t+15 (words 2t, 2t+1).
+  __device__ __forceinline__ u32x4 operand(int j, int t) const {
+    const u32x4 r = v[j][t >> 1];
+    const u32x2 a = unpack8((t & 1) ? r.z : r.x);
+    const u32x2 b = unpack8((t & 1) ? r.w : r.y);
+    return u32x4{a.x, a.y, b.x, b.y};
+  }
+};
+
+template <int N>
+using int_c = std::integral_constant<int, N>;
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(int_c<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// One pass over chunks [c_begin, c_begin + nch) for 32 activation rows.
+//   asrc[2]: this thread's two staging rows (rows a_row and a_row + 16 of the
+//            pass), pointing at element 16 * a_seg of the row;
+//   bptr[2]: the lane's two weight rows (packed bytes, lane-half offset
+//            included);
+//   SWAP:    false -- MFMA A = activations, B = weights: accumulator lane l
+//            holds weight row l % 32 (output column), activation rows
+//            8(i/4) + 4(l/32) + i%4; true -- the operands swapped: lane l
+//            holds activation row l % 32 and weight rows 8(i/4) + 4(l/32) + i%4.
+// Returns the two 32 x 32 int32 tiles (16 x the dot products).
+template <bool SWAP>
+__device__ __forceinline__ void w4a8_pass(const int8_t* const* asrc, int a_row, int a_seg,
+                                          const uint8_t* const* bptr, int c_begin, int nch,
+                                          int rows_pass, int lr, int lh,
+                                          uint8_t (*lds)[32][kLdsRow], i32x16* acc) {
+  constexpr int S = kStages;
+  acc[0] = i32x16{};
+  acc[1] = i32x16{};
+  u32x4 aring[S][2];
+  W4Chunk bring[S];
+
+  auto load_chunk = [&](int i, int slot) __attribute__((always_inline)) {
+    const int64_t c = c_begin + i;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      if (a_row + 16 * sb < rows_pass) {
+        aring[slot][sb] = *reinterpret_cast<const u32x4*>(asrc[sb] + c * kCK);
+      }
+    }
+    bring[slot].load(bptr, c * (kCK / 2));
+  };
+  auto stage_a = [&](int slot, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int r = a_row + 16 * sb;
+      if (r < rows_pass) *reinterpret_cast<u32x4*>(&lds[buf][r][a_seg * 16]) = aring[slot][sb];
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) {
+    if (st < nch) load_chunk(st, st);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  stage_a(0, 0);
+  __syncthreads();
+
+  // Step i: prefetch chunk i+S-1 (only while it exists), multiply chunk i,
+  // stage chunk i+1's activations in the other buffer, barrier.
+  static_assert(S % 2 == 0, "the LDS buffer of chunk i is i % 2 == slot % 2");
+  auto step = [&](int i, auto U, bool prefetch, bool stage) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    if (prefetch) load_chunk(i + S - 1, (u + S - 1) % S);
+    constexpr int buf = u & 1;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&lds[buf][lr][lh * 128 + t * 16]);
+      const u32x4 b0 = bring[u].operand(0, t);
+      const u32x4 b1 = bring[u].operand(1, t);
+      if constexpr (SWAP) {
+        acc[0] = mfma_i8(b0, a, acc[0]);
+        acc[1] = mfma_i8(b1, a, acc[1]);
+      } else {
+        acc[0] = mfma_i8(a, b0, acc[0]);
+        acc[1] = mfma_i8(a, b1, acc[1]);
+      }
+    }
+    if (stage) stage_a((u + 1) % S, buf ^ 1);
+    __syncthreads();
+  };
+  int i0 = 0;
+  for (; i0 + 2 * S - 1 <= nch - 1; i0 += S) {
+    static_for<S>([&](auto U) { step(i0 + U, U, true, true); });
+  }
+  const int rem = nch - i0;
+  static_for<2 * S>([&](auto U) {
+    constexpr int u = decltype(U)::value;
+    if (u < rem) step(i0 + u, int_c<u % S>{}, u + S - 1 < rem, u + 1 < rem);
+  });
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// (float) acc * s_a * s_w, left to right in fp32 (acc: the exact int32 sum).
+__device__ __forceinline__ float dequant(int acc, float sa, float sw) {
+  return __fmul_rn(__fmul_rn(static_cast<float>(acc), sa), sw);
+}
+
+struct W4GroupedArgs {
+  const int8_t* a;          // gate/up: xq [T, kd]; down: hq [P, kd]
+  const float* sa;          // gate/up: sx [T]; down: sh [P]
+  const uint8_t* b0;        // packed weights [E, n, kd/2]
+  const uint8_t* b1;        // gate/up: W_up; down: unused
+  const float* s0;          // row scales of b0 [E * n]
+  const float* s1;
+  uint16_t* c;              // gate/up: h [P, n]; down: expert_out [P, n]
+  const int32_t* sorted_token;
+  const int32_t* group_sizes;
+  const int32_t* group_offsets;
+  const int32_t* group_padded_offsets;
+  const int32_t* block_expert;
+  const int32_t* active_blocks;
+  const int32_t* active_count;
+  int n, kd, block_m, n_tiles;
+};
+
+// Grouped W4A8 GEMM over the active row blocks: workgroup = (row block,
+// column tile), dealt out to XCDs in contiguous ranges; a block's rows run
+// in passes of 32. Gate/up: wave w owns columns 128 nt + 32 w + l%32 of
+// W_gate and W_up (one row of each per lane) and writes
+// h = R(SiLU(g) * u); down: wave w owns columns 256 nt + 64 w + l%32 and
+// + 32 of W_down and writes expert_out.
+template <int DT, bool GATEUP>
+__global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][32][kLdsRow];
+
+  const int total = g.active_count[0] * g.n_tiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
+  const int ab = natural / g.n_tiles;
+  const int nt = natural - ab * g.n_tiles;
+  const int bx = g.active_blocks[ab];
+  const int e = g.block_expert[bx];
+  const int row_in_group = bx * g.block_m - g.group_padded_offsets[e];
+  const int rows = min(g.block_m, g.group_sizes[e] - row_in_group);
+  if (rows <= 0) return;
+  const int m_start = g.group_offsets[e] + row_in_group;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int64_t kd = g.kd;
+
+  int col0;
+  int64_t wrow[2];
+  if constexpr (GATEUP) {
+    col0 = nt * 128 + wave * 32;
+    wrow[0] = static_cast<int64_t>(e) * g.n + col0 + lr;
+    wrow[1] = wrow[0];
+  } else {
+    col0 = nt * 256 + wave * 64;
+    wrow[0] = static_cast<int64_t>(e) * g.n + col0 + lr;
+    wrow[1] = wrow[0] + 32;
+  }
+  const uint8_t* bptr[2] = {g.b0 + wrow[0] * (kd / 2) + lh * 64,
+                            (GATEUP ? g.b1 : g.b0) + wrow[1] * (kd / 2) + lh * 64};
+  const float sw0 = g.s0[wrow[0]];
+  const float sw1 = (GATEUP ? g.s1 : g.s0)[wrow[1]];
+
+  const int a_seg = tid & 15;     // 16-byte segment of a 256-byte row chunk
+  const int a_row = tid >> 4;     // 0..15 (and + 16)
+  const int nch = g.kd / kCK;
+  for (int r0 = 0; r0 < rows; r0 += 32) {
+    if (r0 > 0) __syncthreads();  // every wave is done with the LDS tile
+    const int rows_pass = min(32, rows - r0);
+    const int8_t* asrc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      int r = a_row + 16 * sb;
+      if (r >= rows_pass) r = 0;  // in bounds, never staged
+      const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
+      asrc[sb] = g.a + src * kd + a_seg * 16;
+    }
+    i32x16 acc[2];
+    w4a8_pass<false>(asrc, a_row, a_seg, bptr, 0, nch, rows_pass, lr, lh, lds, acc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = (i >> 2) * 8 + lh * 4 + (i & 3);
+      if (row < rows_pass) {
+        const int64_t out_row = m_start + r0 + row;
+        const float sa = g.sa[GATEUP ? g.sorted_token[out_row] : out_row];
+        uint16_t* out = g.c + out_row * g.n + col0 + lr;
+        const float v0 = dequant(acc[0][i] >> 4, sa, sw0);
+        const float v1 = dequant(acc[1][i] >> 4, sa, sw1);
+        if constexpr (GATEUP) {
+          out[0] = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
+        } else {
+          out[0] = static_cast<uint16_t>(from_float<DT>(v0));
+          out[32] = static_cast<uint16_t>(from_float<DT>(v1));
+        }
+      }
+    }
+  }
+}
+
+// The tutorial's plain W4A8 GEMM: Ct[n, m] = sum_k A[m, k] * B4[n, k], int32,
+// written transposed ([N, M]). Workgroup = (256 columns, chunk range): wave w
+// owns weight rows 256 bx + 64 w + l%32 and + 32; the reduction is split into
+// `splits` ranges of chunks when the column tiles alone cannot fill the GPU,
+// and the partial sums of a split are added with int32 atomics (exact, so
+// the result does not depend on their order). The operands are swapped in
+// the MFMA so that lanes hold consecutive m of one output row.
+__global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(const int8_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ B,
+                                                            int32_t* __restrict__ Ct, int M, int N,
+                                                            int K, int chunks_per_split,
+                                                            int atomic) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][32][kLdsRow];
+  const int col_tile = blockIdx.x;
+  const int split = blockIdx.y;
+  const int nch_total = K / kCK;
+  const int c_begin = split * chunks_per_split;
+  const int nch = min(chunks_per_split, nch_total - c_begin);
+  if (nch <= 0) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int n0 = col_tile * 256 + wave * 64;
+  const uint8_t* bptr[2] = {B + static_cast<int64_t>(n0 + lr) * (K / 2) + lh * 64,
+                            B + static_cast<int64_t>(n0 + 32 + lr) * (K / 2) + lh * 64};
+  const int a_seg = tid & 15;
+  const int a_row = tid >> 4;
+  for (int r0 = 0; r0 < M; r0 += 32) {
+    if (r0 > 0) __syncthreads();
+    const int rows_pass = min(32, M - r0);
+    const int8_t* asrc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      int r = a_row + 16 * sb;
+      if (r >= rows_pass) r = 0;
+      asrc[sb] = A + static_cast<int64_t>(r0 + r) * K + a_seg * 16;
+    }
+    i32x16 acc[2];
+    w4a8_pass<true>(asrc, a_row, a_seg, bptr, c_begin, nch, rows_pass, lr, lh, lds, acc);
+    // lane l: activation row m = r0 + l % 32; weight rows n0 + 32 j + 8(i/4) + 4(l/32) + i%4
+    const int m = r0 + lr;
+    if (m < M) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int n = n0 + 32 * j + (i >> 2) * 8 + lh * 4 + (i & 3);
+          const int v = acc[j][i] >> 4;
+          int32_t* dst = Ct + static_cast<int64_t>(n) * M + m;
+          if (atomic) {
+            atomicAdd(dst, v);
+          } else {
+            *dst = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+__global__ void fill_zero_i32(int32_t* __restrict__ p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// ------------------------------------------------------------ quantizers --
+
+template <int DT>
+__device__ __forceinline__ float load_v(const void* v, int64_t i) {
+  if constexpr (DT == kF32) {
+    return static_cast<const float*>(v)[i];
+  } else {
+    return to_float<DT>(static_cast<const uint16_t*>(v)[i]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float row_scale(const void* v, int64_t base, int cols, int lane,
+                                           float qmax) {
+  float amax = 0.0f;
+  for (int k = lane; k < cols; k += 64) amax = fmaxf(amax, fabsf(load_v<DT>(v, base + k)));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  return amax > 0.0f ? amax / qmax : 1.0f;
+}
+
+__device__ __forceinline__ int quant_code(float v, float s, float qmin, float qmax) {
+  return static_cast<int>(fminf(fmaxf(rintf(v / s), qmin), qmax));
+}
+
+// One wave per row.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_int8_rows_kernel(const void* __restrict__ a,
+                                                                 int64_t rows, int cols,
+                                                                 int8_t* __restrict__ q,
+                                                                 float* __restrict__ scales) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;   // the whole wave exits together
+  const int lane = threadIdx.x & 63;
+  const int64_t base = r * cols;
+  const float s = row_scale<DT>(a, base, cols, lane, 127.0f);
+  if (lane == 0) scales[r] = s;
+  for (int k = lane; k < cols; k += 64) {
+    q[base + k] = static_cast<int8_t>(quant_code(load_v<DT>(a, base + k), s, -127.0f, 127.0f));
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_int4_rows_kernel(const void* __restrict__ w,
+                                                                 int64_t rows, int cols,
+                                                                 uint8_t* __restrict__ packed,
+                                                                 float* __restrict__ scales) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t base = r * cols;
+  const float s = row_scale<DT>(w, base, cols, lane, 7.0f);
+  if (lane == 0) scales[r] = s;
+  const int half = cols / 2;
+  for (int b = lane; b < half; b += 64) {
+    const int q0 = quant_code(load_v<DT>(w, base + 2 * b), s, -8.0f, 7.0f);
+    const int q1 = quant_code(load_v<DT>(w, base + 2 * b + 1), s, -8.0f, 7.0f);
+    packed[r * half + b] = static_cast<uint8_t>((q0 & 0xF) | ((q1 & 0xF) << 4));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_int8_rows(const void* a, int64_t rows, int cols, int dtype, int8_t* q,
+                                     float* scales, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (dtype == kBF16) {
+    hipLaunchKernelGGL(quantize_int8_rows_kernel<kBF16>, grid, dim3(256), 0, stream, a, rows, cols,
+                       q, scales);
+  } else if (dtype == kF16) {
+    hipLaunchKernelGGL(quantize_int8_rows_kernel<kF16>, grid, dim3(256), 0, stream, a, rows, cols,
+                       q, scales);
+  } else {
+    hipLaunchKernelGGL(quantize_int8_rows_kernel<kF32>, grid, dim3(256), 0, stream, a, rows, cols,
+                       q, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int4_rows(const void* w, int64_t rows, int cols, int dtype,
+                                     uint8_t* packed, float* scales, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (dtype == kBF16) {
+    hipLaunchKernelGGL(quantize_int4_rows_kernel<kBF16>, grid, dim3(256), 0, stream, w, rows, cols,
+                       packed, scales);
+  } else if (dtype == kF16) {
+    hipLaunchKernelGGL(quantize_int4_rows_kernel<kF16>, grid, dim3(256), 0, stream, w, rows, cols,
+                       packed, scales);
+  } else {
+    hipLaunchKernelGGL(quantize_int4_rows_kernel<kF32>, grid, dim3(256), 0, stream, w, rows, cols,
+                       packed, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemm(const int8_t* A, const uint8_t* B, int M, int N, int K, int32_t* Ct,
+                            hipStream_t stream) {
+  // Split the reduction while the column tiles give fewer than ~1024
+  // workgroups, keeping at least 2 chunks per split.
+  const int col_tiles = N / 256;
+  const int nch = K / kCK;
+  int per = (static_cast<int64_t>(col_tiles) * nch + 1023) / 1024;
+  per = max(2, per);
+  if (per > nch) per = nch;
+  const int splits = (nch + per - 1) / per;
+  const int atomic = splits > 1 ? 1 : 0;
+  if (atomic) {
+    const int64_t n = static_cast<int64_t>(N) * M;
+    hipLaunchKernelGGL(fill_zero_i32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                       stream, Ct, n);
+  }
+  hipLaunchKernelGGL(w4a8_gemm_kernel, dim3(col_tiles, splits), dim3(kThreads), 0, stream, A, B,
+                     Ct, M, N, K, per, atomic);
+  return hipGetLastError();
+}
+
+template <int DT, bool GATEUP>
+static hipError_t launch_grouped(const W4GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  W4GroupedArgs g;
+  g.a = p.a;
+  g.sa = p.sa;
+  g.b0 = p.b0;
+  g.b1 = p.b1;
+  g.s0 = p.s0;
+  g.s1 = p.s1;
+  g.c = static_cast<uint16_t*>(p.c);
+  g.sorted_token = t.sorted_token;
+  g.group_sizes = t.group_sizes;
+  g.group_offsets = t.group_offsets;
+  g.group_padded_offsets = t.group_padded_offsets;
+  g.block_expert = t.block_expert;
+  g.active_blocks = t.active_blocks;
+  g.active_count = t.active_count;
+  g.n = p.n;
+  g.kd = p.kd;
+  g.block_m = t.block_m;
+  g.n_tiles = p.n / (GATEUP ? 128 : 256);
+  const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
+  const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
+  hipLaunchKernelGGL((w4a8_grouped_kernel<DT, GATEUP>), dim3(grid), dim3(kThreads), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_w4a8(const W4GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  if (p.dtype == kBF16) return launch_grouped<kBF16, true>(p, t, stream);
+  return launch_grouped<kF16, true>(p, t, stream);
+}
+
+hipError_t launch_down_w4a8(const W4GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  if (p.dtype == kBF16) return launch_grouped<kBF16, false>(p, t, stream);
+  return launch_grouped<kF16, false>(p, t, stream);
+}
+
+}  // namespace moe

@@ -143,3 +143,33 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_w4a8_calls_reject_bad_arguments_before_launching():
+    L = _lib.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    # moe_w4a8_gemm(A, B, M, N, K, Ct, stream)
+    assert L.moe_w4a8_gemm(None, fake, 1, 256, 256, fake, None) == 1
+    assert L.moe_w4a8_gemm(fake, fake, 0, 256, 256, fake, None) == 2
+    assert L.moe_w4a8_gemm(fake, fake, 1, 200, 256, fake, None) == 2
+    assert L.moe_w4a8_gemm(fake, fake, 1, 256, 300, fake, None) == 2
+    assert L.moe_w4a8_gemm(fake, fake, 1, 256, 131072 + 256, fake, None) == 2
+    assert "K must be" in L.moe_last_error().decode()
+    # quantizers: odd row length for int4, bad dtype
+    assert L.moe_quantize_int4_rows(fake, 4, 63, 1, fake, fake, None) == 2
+    assert L.moe_quantize_int8_rows(fake, 4, 64, 3, fake, fake, None) == 3
+    assert L.moe_quantize_int8_rows(fake, 0, 64, 1, fake, fake, None) == 0
+    s = _lib.MoeTablesStruct()
+    n = L.moe_tables_bytes(8, 2, 4, 32)
+    assert L.moe_tables_bind(ctypes.byref(s), fake, n, 8, 2, 4, 32) == 0
+    # moe_expert_gate_up_w4a8(xq, sx, wg, wu, sg, su, tables, H, D, dtype, h, stream)
+    assert L.moe_expert_gate_up_w4a8(fake, fake, fake, fake, fake, fake, ctypes.byref(s), 256,
+                                     128, 1, fake, None) == 2          # D % 256
+    assert L.moe_expert_gate_up_w4a8(fake, fake, fake, fake, fake, fake, ctypes.byref(s), 256,
+                                     256, 2, fake, None) == 3          # fp32 output
+    assert L.moe_expert_down_w4a8(fake, None, fake, fake, ctypes.byref(s), 256, 256, 1, fake,
+                                  None) == 1
+    need = L.moe_forward_w4a8_workspace_bytes(8, 2, 256, 256, 1)
+    assert need >= L.moe_forward_workspace_bytes(8, 2, 256, 256, 1) + 8 * 256 + 16 * 256
+    assert L.moe_routed_forward_w4a8(fake, fake, fake, fake, fake, fake, fake, ctypes.byref(s),
+                                     256, 256, 1, fake, need - 1, fake, None) == 5

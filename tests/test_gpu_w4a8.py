@@ -1,0 +1,275 @@
+"""W4A8 on the GPU against the oracle (same seeded inputs).
+
+  * the quantizers (moe_quantize_int8_rows, moe_quantize_int4_rows): codes,
+    packed bytes and scales bit for bit equal to the oracle's, for bf16 /
+    fp16 / fp32 inputs with zero rows, tiny rows and outliers;
+  * the tutorial's plain W4A8 GEMM (moe_w4a8_gemm): int32 results bit-exact
+    at its two serving shapes (M = 1 and M = 32, N = 3584, K = 18944: split
+    reduction with atomics), a single-chunk K (no split), ragged M (several
+    passes of 32 rows) and the extreme operands -128 x -8;
+  * the grouped W4A8 down GEMM (no transcendental in its epilogue): bit-exact
+    expert_out against the oracle's int32 sums dequantised in fp32 in the
+    documented order, at every block_m (passes of 32 rows), ragged groups
+    and masked slots;
+  * the W4A8 forward against the oracle's W4A8 forward: the quantised x bit
+    for bit, h and expert_out per routed pair and y at the graded tolerance
+    (h differs only where SiLU's exponential rounds differently, and then
+    the int8 code of h may differ by one), in full at the mid-size workload
+    and ragged shapes, on sampled tokens at the DeepSeek decode / prefill /
+    skewed workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as S
+from helpers import ORACLE_DT, assert_close_16, gpu_available, metrics, storage
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+DEV = "cuda:0"
+
+
+def _mr():
+    import mixture_experts_routed_moe_amd as mr
+    return mr
+
+
+def _rows_input(dtype, rows, cols, seed):
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randn(rows, cols, generator=g)
+    a[0] = 0.0                                              # zero row
+    a[1] *= 1e-4                                            # tiny row
+    a[2, ::5] *= 300.0                                      # outliers
+    return a.to(dtype).to(DEV)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_quantize_int8_rows_bit_exact(dtype):
+    a = _rows_input(dtype, 37, 2048, 1)
+    q, s = _mr().quantize_int8_rows(a)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_int8_rows(ORACLE_DT[dtype], storage(a))
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_quantize_int4_rows_bit_exact(dtype):
+    w = _rows_input(dtype, 3 * 40, 768, 2).view(3, 40, 768)
+    q = _mr().quantize_int4_rows(w)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_int4_rows(ORACLE_DT[dtype], storage(w))
+    assert np.array_equal(q.packed.cpu().numpy(), rq)
+    assert np.array_equal(q.scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def _gemm_case(M, N, K, seed, extreme=False):
+    g = torch.Generator().manual_seed(seed)
+    if extreme:
+        A = torch.full((M, K), -128, dtype=torch.int8)
+        B = torch.full((N, K // 2), 0x88, dtype=torch.uint8)
+    else:
+        A = torch.randint(-128, 128, (M, K), generator=g, dtype=torch.int16).to(torch.int8)
+        B = torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.int16).to(torch.uint8)
+    Ct = _mr().w4a8_gemm(A.to(DEV), B.to(DEV))
+    torch.cuda.synchronize()
+    return Ct.cpu().numpy(), oracle.w4a8_gemm(A.numpy(), B.numpy())
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 3584, 18944), (32, 3584, 18944), (45, 512, 256),
+                                   (7, 256, 1024), (96, 768, 2048)])
+def test_w4a8_gemm_bit_exact(M, N, K):
+    got, ref = _gemm_case(M, N, K, seed=M * 7 + K)
+    assert got.shape == (N, M)
+    assert np.array_equal(got, ref)
+
+
+def test_w4a8_gemm_extreme_operands():
+    got, ref = _gemm_case(33, 256, 4096, seed=0, extreme=True)
+    assert np.all(ref == 1024 * 4096)
+    assert np.array_equal(got, ref)
+
+
+def test_w4a8_gemm_argument_errors():
+    mr = _mr()
+    A = torch.zeros(4, 512, dtype=torch.int8, device=DEV)
+    B = torch.zeros(200, 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(mr.MoeError, match="MOE_ERR_SHAPE"):
+        mr.w4a8_gemm(A, B)                                  # N not a multiple of 256
+    A = torch.zeros(4, 300, dtype=torch.int8, device=DEV)
+    B = torch.zeros(256, 150, dtype=torch.uint8, device=DEV)
+    with pytest.raises(mr.MoeError, match="MOE_ERR_SHAPE"):
+        mr.w4a8_gemm(A, B)                                  # K not a multiple of 256
+
+
+def _down_case(T, H, D, E, K, block_m, seed, masked=True):
+    """Grouped down GEMM on seeded int8 rows / scales and int4 weights."""
+    mr = _mr()
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    ids[:, 0] = np.where(np.arange(T) % 3 == 0, 1, ids[:, 0])            # a larger group
+    ids[:, 1:] = np.where(ids[:, 1:] == ids[:, :1], -1, ids[:, 1:])
+    if masked:
+        ids[::7, -1] = -1
+    w = rng.uniform(0.1, 1, size=(T, K)).astype(np.float32)
+    P = T * K
+    hq = rng.integers(-127, 128, size=(P, D)).astype(np.int8)
+    sh = rng.uniform(1e-3, 2e-2, size=P).astype(np.float32)
+    wd = (rng.standard_normal((E, H, D)) / np.sqrt(D)).astype(np.float32)
+    packed, sd = oracle.quantize_int4_rows(oracle.F32, wd)
+    tables = mr.moe_dispatch(torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), E,
+                             block_m=block_m)
+    w4 = mr.W4Weights(torch.from_numpy(packed).to(DEV), torch.from_numpy(sd).to(DEV))
+    eo = torch.full((P, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mr.moe_expert_down_w4a8(torch.from_numpy(hq).to(DEV), torch.from_numpy(sh).to(DEV), w4, tables,
+                            torch.bfloat16, expert_out=eo)
+    torch.cuda.synchronize()
+    # expected: per sorted row i of expert e, bf16(float(acc) * sh[i] * sd[e, c])
+    sizes = tables.group_sizes.cpu().numpy()
+    offs = tables.group_offsets.cpu().numpy()
+    got = eo.float().cpu().numpy()
+    n_valid = int(sizes.sum())
+    assert not np.isnan(got[:n_valid]).any()
+    for e in range(E):
+        if sizes[e] == 0:
+            continue
+        rows = slice(offs[e], offs[e] + sizes[e])
+        acc = oracle.w4a8_gemm(hq[rows], packed[e])                       # [H, rows]
+        v = (acc.T.astype(np.float32) * sh[rows, None]) * sd[e][None, :]  # fp32, left to right
+        want = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(got[rows], want), "expert %d" % e
+
+
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
+def test_down_w4a8_bit_exact(block_m):
+    _down_case(T=200, H=512, D=512, E=5, K=3, block_m=block_m, seed=block_m)
+
+
+def _w4_weights(d):
+    mr = _mr()
+    gpu, ref = [], []
+    for n in ("w_gate", "w_up", "w_down"):
+        q = mr.quantize_int4_rows(d[n])
+        torch.cuda.synchronize()
+        rp, rs = oracle.quantize_int4_rows(ORACLE_DT[d[n].dtype], storage(d[n]))
+        assert np.array_equal(q.packed.cpu().numpy(), rp), n
+        assert np.array_equal(q.scales.cpu().numpy().view(np.uint32), rs.view(np.uint32)), n
+        gpu.append(q)
+        ref.append((rp, rs))
+    return gpu, ref
+
+
+def _run_w4(d, gpu, block_m=None):
+    mr = _mr()
+    T, H, D, E = d["T"], d["H"], d["D"], d["E"]
+    tables = mr.moe_dispatch(d["topk_ids"], d["topk_weights"], E, block_m=block_m)
+    ws, h, eo, xq, sx, hq, sh = mr.forward_w4a8_workspace(tables, H, D, d["x"].dtype)
+    h.fill_(float("nan"))
+    eo.fill_(float("nan"))
+    y = torch.full((T, H), float("nan"), dtype=d["x"].dtype, device=DEV)
+    mr.moe_routed_forward_w4a8(d["x"], gpu[0], gpu[1], gpu[2], tables, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    return tables, h, eo, xq, sx, y
+
+
+def _oracle_w4(d, ref, tokens=None, want_pairs=False):
+    (pg, sg), (pu, su), (pd, sd) = ref
+    return oracle.moe_forward_w4a8(ORACLE_DT[d["x"].dtype], storage(d["x"]), pg, pu, pd, sg, su, sd,
+                                   d["topk_ids"].cpu().numpy(), d["topk_weights"].cpu().numpy(),
+                                   tokens=tokens, want_pairs=want_pairs)
+
+
+def _check_x_quant(d, xq, sx):
+    rq, rs = oracle.quantize_int8_rows(ORACLE_DT[d["x"].dtype], storage(d["x"]))
+    assert np.array_equal(xq.cpu().numpy(), rq)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def _check_pairs(tables, h, eo, hp, ep):
+    pos = tables.token_topk_to_pos.cpu().numpy()
+    hg, eg = h.float().cpu().numpy(), eo.float().cpu().numpy()
+    rows = [(pos[s], s) for s in range(pos.size) if pos[s] >= 0]
+    gh = np.stack([hg[p] for p, _ in rows]); rh = np.stack([hp[s] for _, s in rows])
+    ge = np.stack([eg[p] for p, _ in rows]); re = np.stack([ep[s] for _, s in rows])
+    assert not np.isnan(gh).any() and not np.isnan(ge).any()
+    mh, me = metrics(gh, rh), metrics(ge, re)
+    # h: the same int32 sums and fp32 dequantisation; only SiLU's exponential
+    # may round differently (a last-bit flip of a 16-bit value, rarely)
+    assert np.mean(gh != rh) <= 1e-3, ("h mismatch fraction", np.mean(gh != rh))
+    assert mh[0] <= 2e-2 * max(1.0, float(np.abs(rh).max())), ("h", mh)
+    assert me[1] <= 5e-3 and me[0] <= 2e-2 * max(1.0, float(np.abs(re).max())), ("eo", me)
+
+
+def test_forward_w4a8_mid_full():
+    d = S.make_moe_inputs(S.CONFIGS[1], device=DEV)
+    gpu, ref = _w4_weights(d)
+    tables, h, eo, xq, sx, y = _run_w4(d, gpu)
+    _check_x_quant(d, xq, sx)
+    y_ref, hp, ep = _oracle_w4(d, ref, want_pairs=True)
+    assert_close_16(y.float().cpu().numpy(), y_ref, "w4a8 %s" % S.CONFIGS[1]["name"])
+    _check_pairs(tables, h, eo, hp, ep)
+
+
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
+def test_forward_w4a8_ragged(block_m):
+    cfg = dict(name="custom", dtype="bf16", T=300, H=512, D=512, E=5, K=3, renorm=True,
+               zipf=False, seed=41)
+    d = S.make_moe_inputs(cfg, device=DEV)
+    ids = d["topk_ids"].clone()
+    ids[torch.arange(0, 300, 7, device=DEV), 1] = -1         # masked slots
+    ids[:, 0] = torch.where(torch.arange(300, device=DEV) % 3 == 0, 2, ids[:, 0])
+    ids[:, 1:] = torch.where(ids[:, 1:] == ids[:, :1], -1, ids[:, 1:])
+    d["topk_ids"] = ids.contiguous()
+    gpu, ref = _w4_weights(d)
+    tables, h, eo, xq, sx, y = _run_w4(d, gpu, block_m=block_m)
+    y_ref, hp, ep = _oracle_w4(d, ref, want_pairs=True)
+    assert_close_16(y.float().cpu().numpy(), y_ref, "w4a8 ragged bm=%d" % block_m)
+    _check_pairs(tables, h, eo, hp, ep)
+
+
+def test_forward_w4a8_fp16():
+    cfg = dict(name="custom-f16", dtype="f16", T=96, H=256, D=256, E=4, K=2, renorm=False,
+               zipf=False, seed=43)
+    d = S.make_moe_inputs(cfg, device=DEV)
+    gpu, ref = _w4_weights(d)
+    tables, h, eo, xq, sx, y = _run_w4(d, gpu)
+    _check_x_quant(d, xq, sx)
+    y_ref, hp, ep = _oracle_w4(d, ref, want_pairs=True)
+    assert_close_16(y.float().cpu().numpy(), y_ref, "w4a8 fp16")
+    _check_pairs(tables, h, eo, hp, ep)
+
+
+@pytest.mark.parametrize("ci", [2, 3, 4])
+def test_forward_w4a8_full_size_sampled(ci):
+    mr = _mr()
+    cfg = S.CONFIGS[ci]
+    d = S.make_moe_inputs(cfg, device=DEV)
+    gpu, ref = _w4_weights(d)
+    block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"])
+    tables, h, eo, xq, sx, y = _run_w4(d, gpu, block_m=block_m)
+    _check_x_quant(d, xq, sx)
+    rng = np.random.default_rng(ci)
+    tokens = np.sort(rng.choice(cfg["T"], size=16, replace=False)).astype(np.int32)
+    y_ref = _oracle_w4(d, ref, tokens=tokens)
+    got = y.float().cpu().numpy()
+    assert not np.isnan(got).any()
+    assert_close_16(got[tokens], y_ref, "w4a8 %s sampled" % cfg["name"])
+
+
+def test_w4a8_argument_errors():
+    mr = _mr()
+    d = S.make_moe_inputs(S.CONFIGS[1], device=DEV)
+    q = mr.quantize_int4_rows(d["w_gate"])
+    tables = mr.moe_dispatch(d["topk_ids"], d["topk_weights"], d["E"])
+    xq, sx = mr.quantize_int8_rows(d["x"])
+    with pytest.raises(mr.MoeError, match="MOE_ERR_DTYPE"):
+        mr.moe_expert_gate_up_w4a8(xq, sx, d["w_gate"], d["w_up"], tables)
+    with pytest.raises(mr.MoeError, match="MOE_ERR_DTYPE"):
+        mr.moe_expert_gate_up_w4a8(xq, sx, q, q, tables, dtype=torch.float32)
+    with pytest.raises(mr.MoeError, match="MOE_ERR_SHAPE"):
+        mr.W4Weights(q.packed, q.scales[:, :-1].contiguous())
+    with pytest.raises(mr.MoeError, match="MOE_ERR_SHAPE"):
+        mr.moe_expert_gate_up_w4a8(xq[:-1], sx[:-1], q, q, tables)
