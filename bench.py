@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MFMA_INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pmc_grouped_gemm_gate_up_deepseek_decode.md")
 GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", f)
@@ -77,35 +78,45 @@ def counter_traffic():
     return float(val.group(1))
 
 
-def workload_numbers(d, tables_sizes, fp8_weights=False):
+def workload_numbers(d, tables_sizes, weights="16bit"):
     """Algorithmic FLOPs and bytes of one step, per kernel (units in the
-    design notes): weights of the experts that receive rows once (FP8
-    weights: 1 byte each plus a 4-byte scale per row), x read once, h /
-    expert_out written and read once, y written once."""
+    design notes): weights of the experts that receive rows once (FP8: 1
+    byte each, W4A8: half a byte, plus a 4-byte scale per row), x read once,
+    h / expert_out written and read once, y written once; W4A8 adds the int8
+    copies of x and h (and their scales), written once and read once."""
     T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
     b = d["x"].element_size()
-    wb = 1 if fp8_weights else b
-    sc = 4 if fp8_weights else 0          # scale bytes per weight row
+    wb = {"16bit": b, "fp8": 1, "w4a8": 0.5}[weights]
+    sc = 0 if weights == "16bit" else 4   # scale bytes per weight row
     n_valid = int(tables_sizes.sum())
     e_active = int((tables_sizes > 0).sum())
     P = T * K
-    gate_up_bytes = e_active * 2 * D * (H * wb + sc) + T * H * b + n_valid * D * b
-    down_bytes = e_active * H * (D * wb + sc) + n_valid * D * b + n_valid * H * b
-    reduce_bytes = n_valid * H * b + T * H * b + P * 8
-    dispatch_bytes = P * 8 + n_valid * 12 + P * 8 + 12 * E
-    flops_gate_up = 4 * n_valid * H * D
-    flops_down = 2 * n_valid * H * D
-    b_min = e_active * 3 * H * D * wb + e_active * (2 * D + H) * sc + 2 * T * H * b + P * 8
-    return dict(n_valid=n_valid, e_active=e_active, gate_up_bytes=gate_up_bytes,
-                down_bytes=down_bytes, reduce_bytes=reduce_bytes, dispatch_bytes=dispatch_bytes,
-                flops_gate_up=flops_gate_up, flops_down=flops_down,
-                flops=flops_gate_up + flops_down, b_min=b_min)
+    w_gate_up = int(e_active * 2 * D * (H * wb + sc))
+    w_down = int(e_active * H * (D * wb + sc))
+    out = dict(n_valid=n_valid, e_active=e_active)
+    if weights == "w4a8":
+        out["quant_x_bytes"] = T * H * b + T * H + T * 4
+        out["gate_up_bytes"] = w_gate_up + T * H + T * 4 + n_valid * D * b
+        out["quant_h_bytes"] = P * D * b + P * D + P * 4
+        out["down_bytes"] = w_down + n_valid * D + n_valid * 4 + n_valid * H * b
+    else:
+        out["gate_up_bytes"] = w_gate_up + T * H * b + n_valid * D * b
+        out["down_bytes"] = w_down + n_valid * D * b + n_valid * H * b
+    out["reduce_bytes"] = n_valid * H * b + T * H * b + P * 8
+    out["dispatch_bytes"] = P * 8 + n_valid * 12 + P * 8 + 12 * E
+    out["flops_gate_up"] = 4 * n_valid * H * D
+    out["flops_down"] = 2 * n_valid * H * D
+    out["flops"] = out["flops_gate_up"] + out["flops_down"]
+    out["b_min"] = w_gate_up + w_down + 2 * T * H * b + P * 8
+    return out
 
 
-def time_workload(cfg, steps, warmup, block_m, dev, fp8_weights=False):
-    """One workload's step timed kernel by kernel. fp8_weights: the expert
-    weights are quantized once (moe_quantize_fp8_rows, timed on its own, not
-    part of the step) and the step runs the FP8-weight GEMMs."""
+def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit"):
+    """One workload's step timed kernel by kernel. weights "fp8" / "w4a8":
+    the expert weights are quantized once (moe_quantize_fp8_rows /
+    moe_quantize_int4_rows, timed on its own, not part of the step) and the
+    step runs the FP8-weight GEMMs, or the W4A8 path (x and h quantised to
+    int8 inside the step, each a timed kernel of its own)."""
     import torch
 
     import mixture_experts_routed_moe_amd as mr
@@ -116,10 +127,11 @@ def time_workload(cfg, steps, warmup, block_m, dev, fp8_weights=False):
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
     quant_ms = None
-    if fp8_weights:
+    if weights != "16bit":
+        qfn = mr.quantize_fp8_rows if weights == "fp8" else mr.quantize_int4_rows
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
-        q = [mr.quantize_fp8_rows(d[n]) for n in ("w_gate", "w_up", "w_down")]
+        q = [qfn(d[n]) for n in ("w_gate", "w_up", "w_down")]
         ev[1].record()
         torch.cuda.synchronize()
         quant_ms = ev[0].elapsed_time(ev[1])
@@ -129,7 +141,12 @@ def time_workload(cfg, steps, warmup, block_m, dev, fp8_weights=False):
     ids, w = d["topk_ids"], d["topk_weights"]
     x, wg, wu, wd = d["x"], d["w_gate"], d["w_up"], d["w_down"]
     tables = mr.MoeTables(T, K, E, block_m, dev)
-    ws, h, eo = mr.forward_workspace(tables, H, D, x.dtype)
+    if weights == "w4a8":
+        ws, h, eo, xq, sx, hq, sh = mr.forward_w4a8_workspace(tables, H, D, x.dtype)
+        names = ["dispatch", "quant_x", "gate_up", "quant_h", "down", "reduce"]
+    else:
+        ws, h, eo = mr.forward_workspace(tables, H, D, x.dtype)
+        names = ["dispatch", "gate_up", "down", "reduce"]
     y = torch.empty(T, H, dtype=x.dtype, device=dev)
     pos = tables.token_topk_to_pos.view(T, K)
     wt = tables.topk_weights.view(T, K)
@@ -138,19 +155,29 @@ def time_workload(cfg, steps, warmup, block_m, dev, fp8_weights=False):
         ev[0].record()
         mr.moe_dispatch(ids, w, E, block_m=block_m, tables=tables)
         ev[1].record()
-        if fp8_weights:
-            mr.moe_expert_gate_up_w8(x, wg, wu, tables, h=h)
+        if weights == "w4a8":
+            mr.quantize_int8_rows(x, q=xq, scales=sx)
             ev[2].record()
-            mr.moe_expert_down_w8(h, wd, tables, expert_out=eo)
+            mr.moe_expert_gate_up_w4a8(xq, sx, wg, wu, tables, x.dtype, h=h)
+            ev[3].record()
+            mr.quantize_int8_rows(h, q=hq, scales=sh)
+            ev[4].record()
+            mr.moe_expert_down_w4a8(hq, sh, wd, tables, x.dtype, expert_out=eo)
+            ev[5].record()
         else:
-            mr.moe_expert_gate_up(x, wg, wu, tables, h=h)
-            ev[2].record()
-            mr.moe_expert_down(h, wd, tables, expert_out=eo)
-        ev[3].record()
+            if weights == "fp8":
+                mr.moe_expert_gate_up_w8(x, wg, wu, tables, h=h)
+                ev[2].record()
+                mr.moe_expert_down_w8(h, wd, tables, expert_out=eo)
+            else:
+                mr.moe_expert_gate_up(x, wg, wu, tables, h=h)
+                ev[2].record()
+                mr.moe_expert_down(h, wd, tables, expert_out=eo)
+            ev[3].record()
         mr.moe_reduce_fused(eo, pos, wt, y=y)
-        ev[4].record()
+        ev[len(names)].record()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
     for _ in range(warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -161,14 +188,13 @@ def time_workload(cfg, steps, warmup, block_m, dev, fp8_weights=False):
         step(events[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    names = ["dispatch", "gate_up", "down", "reduce"]
     per = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps
            for j, n in enumerate(names)}
-    span = sum(ev[0].elapsed_time(ev[4]) for ev in events) / steps
+    span = sum(ev[0].elapsed_time(ev[len(names)]) for ev in events) / steps
     sizes = tables.group_sizes.cpu()
-    nums = workload_numbers(d, sizes, fp8_weights)
+    nums = workload_numbers(d, sizes, weights)
     return dict(d=d, tables=tables, block_m=block_m, wall_ms=wall_ms, event_ms=span,
-                kernel_ms=per, nums=nums, gen_s=t_gen, quant_ms=quant_ms)
+                kernel_ms=per, nums=nums, gen_s=t_gen, quant_ms=quant_ms, weights=weights)
 
 
 def summarize(r):
@@ -176,20 +202,23 @@ def summarize(r):
     ms = r["wall_ms"]
     gbs = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
     kernels = {}
-    for n, key in (("dispatch", "dispatch_bytes"), ("gate_up", "gate_up_bytes"),
-                   ("down", "down_bytes"), ("reduce", "reduce_bytes")):
+    for n in per:
+        key = n + "_bytes"
         kernels[n] = {"ms": round(per[n], 4), "algo_bytes": nums[key],
                       "GB_s": round(gbs(nums[key], per[n]), 1),
                       "hbm_frac": round(gbs(nums[key], per[n]) / HBM_PEAK_GBS, 4)}
     for n, key in (("gate_up", "flops_gate_up"), ("down", "flops_down")):
-        kernels[n]["TFLOP_s"] = round(nums[key] / (per[n] * 1e-3) / 1e12, 2)
+        kernels[n]["TFLOP_s" if r.get("weights") != "w4a8" else "TOP_s"] = \
+            round(nums[key] / (per[n] * 1e-3) / 1e12, 2)
+    # W4A8 runs int8 MFMA (5.0 POP/s dense); the others bf16 / fp16 MFMA
+    peak = MFMA_INT8_PEAK_TOPS if r.get("weights") == "w4a8" else MFMA_BF16_PEAK_TFLOPS
     tflops = nums["flops"] / (ms * 1e-3) / 1e12
     hbm = gbs(nums["b_min"], ms)
-    t_roof_ms = max(nums["b_min"] / (HBM_PEAK_GBS * 1e9), nums["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    t_roof_ms = max(nums["b_min"] / (HBM_PEAK_GBS * 1e9), nums["flops"] / (peak * 1e12)) * 1e3
     return dict(ms_per_layer=round(ms, 4), event_ms_per_layer=round(r["event_ms"], 4),
                 TFLOP_s=round(tflops, 2), HBM_GB_s=round(hbm, 1),
                 hbm_frac=round(hbm / HBM_PEAK_GBS, 4),
-                mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                mfma_frac=round(tflops / peak, 4),
                 roofline_frac=round(t_roof_ms / ms, 4), roofline_ms=round(t_roof_ms, 4),
                 flops=nums["flops"], b_min_bytes=nums["b_min"], n_valid=nums["n_valid"],
                 active_experts=nums["e_active"], block_m=r["block_m"], kernels=kernels)
@@ -210,6 +239,31 @@ def _time_rotating(fn, inputs, steps, warmup):
     ev[1].record()
     torch.cuda.synchronize()
     return ev[0].elapsed_time(ev[1]) / steps
+
+
+def time_w4a8_gemm(steps, warmup, dev):
+    """The plain W4A8 GEMM (moe_w4a8_gemm) at the tutorial's two serving
+    shapes, N = 3584, K = 18944: M = 1 (a GEMV-like decode step) and M = 32
+    (a small batch). Seeded int8 A and random packed int4 B; 10 copies of B
+    rotate so each call reads its weights from HBM."""
+    import torch
+
+    import mixture_experts_routed_moe_amd as mr
+    out = []
+    N, K = 3584, 18944
+    g = torch.Generator(device=dev).manual_seed(11)
+    Bs = [torch.randint(0, 256, (N, K // 2), generator=g, device=dev, dtype=torch.int16)
+          .to(torch.uint8) for _ in range(10)]
+    for name, M in (("gemv_like", 1), ("small_batch", 32)):
+        A = torch.randint(-127, 128, (M, K), generator=g, device=dev, dtype=torch.int16).to(torch.int8)
+        Ct = torch.empty((N, M), dtype=torch.int32, device=dev)
+        ms = _time_rotating(lambda B: mr.w4a8_gemm(A, B, Ct=Ct), Bs, steps, warmup)
+        nbytes = N * K // 2 + M * K + N * M * 4
+        out.append({"workload": "W4A8 GEMM %s M=%d N=%d K=%d" % (name, M, N, K),
+                    "us": round(ms * 1e3, 2), "algo_bytes": nbytes,
+                    "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    return out
 
 
 def time_reduce(steps, warmup, dev):
@@ -456,7 +510,7 @@ def main():
         torch.cuda.empty_cache()
         fp8 = {}
         for ci in (2, 3):
-            r8 = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev, fp8_weights=True)
+            r8 = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev, weights="fp8")
             r8.pop("d")
             r8.pop("tables")
             torch.cuda.empty_cache()
@@ -465,6 +519,20 @@ def main():
             s8["workload"] = S.CONFIGS[ci]["name"] + " with FP8 E4M3 expert weights (per-row scales)"
             fp8["T%d" % S.CONFIGS[ci]["T"]] = s8
         extras["fp8_weights"] = fp8
+        w4 = {}
+        for ci in (2, 3):
+            r4 = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev, weights="w4a8")
+            r4.pop("d")
+            r4.pop("tables")
+            torch.cuda.empty_cache()
+            s4 = summarize(r4)
+            s4["quantize_ms"] = round(r4["quant_ms"], 3)
+            s4["workload"] = (S.CONFIGS[ci]["name"] + " with W4A8 experts (int4 weights, per-row "
+                              "scales; int8 activations, per-row scales)")
+            w4["T%d" % S.CONFIGS[ci]["T"]] = s4
+        extras["w4a8"] = w4
+        extras["w4a8_gemm"] = time_w4a8_gemm(args.steps, args.warmup, dev)
+        torch.cuda.empty_cache()
         print("# %s" % json.dumps(extras), file=sys.stderr, flush=True)
 
     gu = main_s["kernels"]["gate_up"]
@@ -497,6 +565,8 @@ def main():
         "mfma_probe": extras.get("mfma_probe"),
         "gate": extras.get("gate"),
         "fp8_weights": extras.get("fp8_weights"),
+        "w4a8": extras.get("w4a8"),
+        "w4a8_gemm": extras.get("w4a8_gemm"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

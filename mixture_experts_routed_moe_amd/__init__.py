@@ -365,14 +365,21 @@ class W4Weights:
         return 3
 
 
-def quantize_int8_rows(a):
+def quantize_int8_rows(a, q=None, scales=None):
     """moe_quantize_int8_rows on a [rows, cols] (fp16 / bf16 / fp32): int8
-    codes in [-127, 127] and fp32 scales amax / 127. Returns (q, scales)."""
+    codes in [-127, 127] and fp32 scales amax / 127. Returns (q, scales)
+    (written into q / scales when given)."""
     _check_tensor(a, "a", None, 2)
     _require(a.dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "a must be float16, bfloat16 or float32")
     rows, cols = a.shape
-    q = torch.empty((rows, cols), dtype=torch.int8, device=a.device)
-    scales = torch.empty((rows,), dtype=torch.float32, device=a.device)
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=a.device)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=a.device)
+    _check_tensor(q, "q", torch.int8, 2, a.device)
+    _check_tensor(scales, "scales", torch.float32, 1, a.device)
+    _require(tuple(q.shape) == (rows, cols) and scales.shape[0] == rows, MOE_ERR_SHAPE,
+             "q must be [%d, %d] and scales [%d]" % (rows, cols, rows))
     check(lib().moe_quantize_int8_rows(_ptr(a), rows, cols, _DTYPE_CODE[a.dtype], _ptr(q),
                                        _ptr(scales), _stream(a.device)))
     return q, scales

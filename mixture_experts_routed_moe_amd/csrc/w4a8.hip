@@ -41,7 +41,20 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;
 constexpr int kCK = 256;                 // reduction elements per chunk
 constexpr int kLdsRow = kCK + 16;        // bytes per LDS A row (16 bytes of padding)
-constexpr int kStages = 4;               // weight chunks in the register ring
+#ifndef MOE_W4_STAGES
+#define MOE_W4_STAGES 2
+#endif
+#ifndef MOE_W4_GEMM_WG
+#define MOE_W4_GEMM_WG 256
+#endif
+#ifndef MOE_W4_GEMM_STAGES
+#define MOE_W4_GEMM_STAGES 4
+#endif
+#ifndef MOE_W4_WIDE_NA
+#define MOE_W4_WIDE_NA 4
+#endif
+constexpr int kStages = MOE_W4_STAGES;   // weight chunks in the register ring
+constexpr int kGemmStages = MOE_W4_GEMM_STAGES;   // the same for the plain GEMM
 
 __device__ __forceinline__ i32x16 mfma_i8(u32x4 a, u32x4 b, i32x16 c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
@@ -91,42 +104,43 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// One pass over chunks [c_begin, c_begin + nch) for 32 activation rows.
-//   asrc[2]: this thread's two staging rows (rows a_row and a_row + 16 of the
-//            pass), pointing at element 16 * a_seg of the row;
+// One pass over chunks [c_begin, c_begin + nch) for NA groups of 32
+// activation rows (the LDS tile holds 32 * NAS rows, NAS >= NA).
+//   asrc[2q + sb]: this thread's staging row of group q (row 32q + a_row +
+//            16 sb of the pass), pointing at element 16 * a_seg of the row;
 //   bptr[2]: the lane's two weight rows (packed bytes, lane-half offset
-//            included);
+//            included); each unpacked weight operand feeds the NA groups;
 //   SWAP:    false -- MFMA A = activations, B = weights: accumulator lane l
 //            holds weight row l % 32 (output column), activation rows
-//            8(i/4) + 4(l/32) + i%4; true -- the operands swapped: lane l
-//            holds activation row l % 32 and weight rows 8(i/4) + 4(l/32) + i%4.
-// Returns the two 32 x 32 int32 tiles (16 x the dot products).
-template <bool SWAP>
+//            8(i/4) + 4(l/32) + i%4 of the group; true -- the operands
+//            swapped: lane l holds activation row l % 32 and weight rows
+//            8(i/4) + 4(l/32) + i%4.
+// acc[2q + j]: group q against weight row j (16 x the dot products).
+template <bool SWAP, int NA, int NAS, int S>
 __device__ __forceinline__ void w4a8_pass(const int8_t* const* asrc, int a_row, int a_seg,
                                           const uint8_t* const* bptr, int c_begin, int nch,
                                           int rows_pass, int lr, int lh,
-                                          uint8_t (*lds)[32][kLdsRow], i32x16* acc) {
-  constexpr int S = kStages;
-  acc[0] = i32x16{};
-  acc[1] = i32x16{};
-  u32x4 aring[S][2];
+                                          uint8_t (*lds)[32 * NAS][kLdsRow], i32x16* acc) {
+#pragma unroll
+  for (int q = 0; q < 2 * NA; ++q) acc[q] = i32x16{};
+  u32x4 aring[S][2 * NA];
   W4Chunk bring[S];
 
   auto load_chunk = [&](int i, int slot) __attribute__((always_inline)) {
     const int64_t c = c_begin + i;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      if (a_row + 16 * sb < rows_pass) {
-        aring[slot][sb] = *reinterpret_cast<const u32x4*>(asrc[sb] + c * kCK);
+    for (int q = 0; q < 2 * NA; ++q) {
+      if (a_row + 16 * q < rows_pass) {
+        aring[slot][q] = *reinterpret_cast<const u32x4*>(asrc[q] + c * kCK);
       }
     }
     bring[slot].load(bptr, c * (kCK / 2));
   };
   auto stage_a = [&](int slot, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int r = a_row + 16 * sb;
-      if (r < rows_pass) *reinterpret_cast<u32x4*>(&lds[buf][r][a_seg * 16]) = aring[slot][sb];
+    for (int q = 0; q < 2 * NA; ++q) {
+      const int r = a_row + 16 * q;
+      if (r < rows_pass) *reinterpret_cast<u32x4*>(&lds[buf][r][a_seg * 16]) = aring[slot][q];
     }
   };
 
@@ -147,15 +161,18 @@ __device__ __forceinline__ void w4a8_pass(const int8_t* const* asrc, int a_row, 
     constexpr int buf = u & 1;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&lds[buf][lr][lh * 128 + t * 16]);
       const u32x4 b0 = bring[u].operand(0, t);
       const u32x4 b1 = bring[u].operand(1, t);
-      if constexpr (SWAP) {
-        acc[0] = mfma_i8(b0, a, acc[0]);
-        acc[1] = mfma_i8(b1, a, acc[1]);
-      } else {
-        acc[0] = mfma_i8(a, b0, acc[0]);
-        acc[1] = mfma_i8(a, b1, acc[1]);
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&lds[buf][32 * q + lr][lh * 128 + t * 16]);
+        if constexpr (SWAP) {
+          acc[2 * q] = mfma_i8(b0, a, acc[2 * q]);
+          acc[2 * q + 1] = mfma_i8(b1, a, acc[2 * q + 1]);
+        } else {
+          acc[2 * q] = mfma_i8(a, b0, acc[2 * q]);
+          acc[2 * q + 1] = mfma_i8(a, b1, acc[2 * q + 1]);
+        }
       }
     }
     if (stage) stage_a((u + 1) % S, buf ^ 1);
@@ -199,13 +216,13 @@ struct W4GroupedArgs {
 
 // Grouped W4A8 GEMM over the active row blocks: workgroup = (row block,
 // column tile), dealt out to XCDs in contiguous ranges; a block's rows run
-// in passes of 32. Gate/up: wave w owns columns 128 nt + 32 w + l%32 of
-// W_gate and W_up (one row of each per lane) and writes
-// h = R(SiLU(g) * u); down: wave w owns columns 256 nt + 64 w + l%32 and
-// + 32 of W_down and writes expert_out.
-template <int DT, bool GATEUP>
+// in passes of up to 32 * NAMAX rows (the weights stream once per pass).
+// Gate/up: wave w owns columns 128 nt + 32 w + l%32 of W_gate and W_up (one
+// row of each per lane) and writes h = R(SiLU(g) * u); down: wave w owns
+// columns 256 nt + 64 w + l%32 and + 32 of W_down and writes expert_out.
+template <int DT, bool GATEUP, int NAMAX>
 __global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][32][kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][32 * NAMAX][kLdsRow];
 
   const int total = g.active_count[0] * g.n_tiles;
   const int per_xcd = (total + 7) >> 3;
@@ -244,38 +261,49 @@ __global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g)
   const float sw1 = (GATEUP ? g.s1 : g.s0)[wrow[1]];
 
   const int a_seg = tid & 15;     // 16-byte segment of a 256-byte row chunk
-  const int a_row = tid >> 4;     // 0..15 (and + 16)
+  const int a_row = tid >> 4;     // 0..15 (+ 16 sb + 32 q)
   const int nch = g.kd / kCK;
-  for (int r0 = 0; r0 < rows; r0 += 32) {
+  for (int r0 = 0; r0 < rows; r0 += 32 * NAMAX) {
     if (r0 > 0) __syncthreads();  // every wave is done with the LDS tile
-    const int rows_pass = min(32, rows - r0);
-    const int8_t* asrc[2];
+    const int rows_pass = min(32 * NAMAX, rows - r0);
+    const int8_t* asrc[2 * NAMAX];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      int r = a_row + 16 * sb;
+    for (int q = 0; q < 2 * NAMAX; ++q) {
+      int r = a_row + 16 * q;
       if (r >= rows_pass) r = 0;  // in bounds, never staged
       const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
-      asrc[sb] = g.a + src * kd + a_seg * 16;
+      asrc[q] = g.a + src * kd + a_seg * 16;
     }
-    i32x16 acc[2];
-    w4a8_pass<false>(asrc, a_row, a_seg, bptr, 0, nch, rows_pass, lr, lh, lds, acc);
+    i32x16 acc[2 * NAMAX];
+    auto epilogue = [&](auto NAC) __attribute__((always_inline)) {
+      constexpr int na = decltype(NAC)::value;
+      w4a8_pass<false, na, NAMAX, kStages>(asrc, a_row, a_seg, bptr, 0, nch, rows_pass, lr, lh, lds, acc);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = (i >> 2) * 8 + lh * 4 + (i & 3);
-      if (row < rows_pass) {
-        const int64_t out_row = m_start + r0 + row;
-        const float sa = g.sa[GATEUP ? g.sorted_token[out_row] : out_row];
-        uint16_t* out = g.c + out_row * g.n + col0 + lr;
-        const float v0 = dequant(acc[0][i] >> 4, sa, sw0);
-        const float v1 = dequant(acc[1][i] >> 4, sa, sw1);
-        if constexpr (GATEUP) {
-          out[0] = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
-        } else {
-          out[0] = static_cast<uint16_t>(from_float<DT>(v0));
-          out[32] = static_cast<uint16_t>(from_float<DT>(v1));
+      for (int q = 0; q < na; ++q) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 32 * q + (i >> 2) * 8 + lh * 4 + (i & 3);
+          if (row < rows_pass) {
+            const int64_t out_row = m_start + r0 + row;
+            const float sa = g.sa[GATEUP ? g.sorted_token[out_row] : out_row];
+            uint16_t* out = g.c + out_row * g.n + col0 + lr;
+            const float v0 = dequant(acc[2 * q][i] >> 4, sa, sw0);
+            const float v1 = dequant(acc[2 * q + 1][i] >> 4, sa, sw1);
+            if constexpr (GATEUP) {
+              out[0] = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
+            } else {
+              out[0] = static_cast<uint16_t>(from_float<DT>(v0));
+              out[32] = static_cast<uint16_t>(from_float<DT>(v1));
+            }
+          }
         }
       }
-    }
+    };
+    const int active = (rows_pass + 31) >> 5;
+    static_for<NAMAX>([&](auto I) {
+      constexpr int na = decltype(I)::value + 1;
+      if (active == na) epilogue(int_c<na>{});
+    });
   }
 }
 
@@ -320,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(const int8_t* __res
       asrc[sb] = A + static_cast<int64_t>(r0 + r) * K + a_seg * 16;
     }
     i32x16 acc[2];
-    w4a8_pass<true>(asrc, a_row, a_seg, bptr, c_begin, nch, rows_pass, lr, lh, lds, acc);
+    w4a8_pass<true, 1, 1, kGemmStages>(asrc, a_row, a_seg, bptr, c_begin, nch, rows_pass, lr, lh, lds, acc);
     // lane l: activation row m = r0 + l % 32; weight rows n0 + 32 j + 8(i/4) + 4(l/32) + i%4
     const int m = r0 + lr;
     if (m < M) {
@@ -444,11 +472,12 @@ hipError_t launch_quantize_int4_rows(const void* w, int64_t rows, int cols, int 
 
 hipError_t launch_w4a8_gemm(const int8_t* A, const uint8_t* B, int M, int N, int K, int32_t* Ct,
                             hipStream_t stream) {
-  // Split the reduction while the column tiles give fewer than ~1024
-  // workgroups, keeping at least 2 chunks per split.
+  // Split the reduction while the column tiles give fewer than
+  // MOE_W4_GEMM_WG workgroups, keeping at least 2 chunks per split.
   const int col_tiles = N / 256;
   const int nch = K / kCK;
-  int per = (static_cast<int64_t>(col_tiles) * nch + 1023) / 1024;
+  int per = static_cast<int>((static_cast<int64_t>(col_tiles) * nch + MOE_W4_GEMM_WG - 1) /
+                             MOE_W4_GEMM_WG);
   per = max(2, per);
   if (per > nch) per = nch;
   const int splits = (nch + per - 1) / per;
@@ -486,7 +515,17 @@ static hipError_t launch_grouped(const W4GemmProblem& p, const moe_tables& t, hi
   g.n_tiles = p.n / (GATEUP ? 128 : 256);
   const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
   const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
-  hipLaunchKernelGGL((w4a8_grouped_kernel<DT, GATEUP>), dim3(grid), dim3(kThreads), 0, stream, g);
+  // Row groups per pass: 1 for decode-sized blocks (two workgroups per CU),
+  // 2 for 64-row blocks, 4 (two passes of 128 rows) for 128- and 256-row
+  // blocks.
+  if (t.block_m <= 32) {
+    hipLaunchKernelGGL((w4a8_grouped_kernel<DT, GATEUP, 1>), dim3(grid), dim3(kThreads), 0, stream, g);
+  } else if (t.block_m == 64) {
+    hipLaunchKernelGGL((w4a8_grouped_kernel<DT, GATEUP, 2>), dim3(grid), dim3(kThreads), 0, stream, g);
+  } else {
+    hipLaunchKernelGGL((w4a8_grouped_kernel<DT, GATEUP, MOE_W4_WIDE_NA>), dim3(grid), dim3(kThreads),
+                       0, stream, g);
+  }
   return hipGetLastError();
 }
 
