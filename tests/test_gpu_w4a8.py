@@ -47,8 +47,9 @@ def _rows_input(dtype, rows, cols, seed):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
-def test_quantize_int8_rows_bit_exact(dtype):
-    a = _rows_input(dtype, 37, 2048, 1)
+@pytest.mark.parametrize("cols", [2048, 7168, 2044])      # 2044: the scalar path
+def test_quantize_int8_rows_bit_exact(dtype, cols):
+    a = _rows_input(dtype, 37, cols, 1)
     q, s = _mr().quantize_int8_rows(a)
     torch.cuda.synchronize()
     rq, rs = oracle.quantize_int8_rows(ORACLE_DT[dtype], storage(a))
