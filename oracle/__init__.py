@@ -52,6 +52,10 @@ def lib():
         L.oracle_quantize_int8_rows.argtypes = [i32, vp, i64, i32, vp, f32p]
         L.oracle_quantize_int4_rows.argtypes = [i32, vp, i64, i32, vp, f32p]
         L.oracle_w4a8_gemm.argtypes = [vp, vp, i32, i32, i32, vp]
+        L.oracle_quantize_mx_rows.argtypes = [i32, vp, i64, i32, i32, vp, vp]
+        L.oracle_mx_decode.argtypes = [vp, vp, i64, i32, i32, f32p]
+        L.oracle_moe_forward_mx.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, i32p, f32p, i32, i32,
+                                            i32, i32, i32, i32p, i32, f32p, f32p, f32p]
         L.oracle_moe_forward_w4a8.argtypes = [i32, vp, vp, vp, vp, f32p, f32p, f32p, i32p, f32p,
                                               i32, i32, i32, i32, i32, i32p, i32, f32p, f32p, f32p]
         _lib = L
@@ -311,4 +315,54 @@ def moe_forward_w4a8(dt, x, wg4, wu4, wd4, sg, su, sd, ids, w, tokens=None, want
     rc = lib().oracle_moe_forward_w4a8(dt, _ptr(xs), *[_ptr(a) for a in args], _ptr(ids), _ptr(w),
                                        T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
     assert rc == 0, "oracle_moe_forward_w4a8 rejected its arguments"
+    return (y, hp, ep) if want_pairs else y
+
+
+MX_FP8, MX_FP4 = 0, 4
+
+
+def quantize_mx_rows(dt, v, fmt):
+    """oracle_quantize_mx_rows: MX codes and E8M0 scales (blocks of 32 along
+    the last axis). fmt MX_FP8 -> E4M3 codes of v's shape; MX_FP4 -> packed
+    E2M1 [..., cols/2]. Returns (codes uint8, scales uint8 [..., cols/32])."""
+    vs = _storage(np.asarray(v), dt)
+    cols = vs.shape[-1]
+    rows = vs.size // cols
+    cshape = vs.shape if fmt == MX_FP8 else vs.shape[:-1] + (cols // 2,)
+    codes = np.empty(cshape, np.uint8)
+    scales = np.empty(vs.shape[:-1] + (cols // 32,), np.uint8)
+    assert lib().oracle_quantize_mx_rows(dt, _ptr(vs), rows, cols, fmt, _ptr(codes), _ptr(scales)) == 0
+    return codes, scales
+
+
+def mx_decode(codes, scales, fmt):
+    """oracle_mx_decode: the fp32 values X * element of MX rows."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    cols = scales.shape[-1] * 32
+    rows = scales.size // scales.shape[-1]
+    out = np.empty(scales.shape[:-1] + (cols,), np.float32)
+    assert lib().oracle_mx_decode(_ptr(codes), _ptr(scales), rows, cols, fmt, _ptr(out)) == 0
+    return out
+
+
+def moe_forward_mx(dt, x, wg, wu, wd, sg, su, sd, ids, w, tokens=None, want_pairs=False):
+    """oracle_moe_forward_mx: MXFP4 expert weights (packed [E, D, H/2] /
+    [E, D, H/2] / [E, H, D/2], E8M0 scales [E, D, H/32] / [E, D, H/32] /
+    [E, H, D/32]) against MXFP8 activations. Same outputs as moe_forward."""
+    xs = _storage(x, dt)
+    T, H = xs.shape
+    E, D, _ = wg.shape
+    K = ids.shape[1]
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tokens is None else len(tok)
+    y = np.empty((n, H), np.float32)
+    hp = np.empty((n * K, D), np.float32) if want_pairs else None
+    ep = np.empty((n * K, H), np.float32) if want_pairs else None
+    args = [_c(a, np.uint8) for a in (wg, wu, wd, sg, su, sd)]
+    rc = lib().oracle_moe_forward_mx(dt, _ptr(xs), *[_ptr(a) for a in args], _ptr(ids), _ptr(w),
+                                     T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
+    assert rc == 0, "oracle_moe_forward_mx rejected its arguments"
     return (y, hp, ep) if want_pairs else y

@@ -601,6 +601,190 @@ int oracle_moe_forward_w4a8(int dt, const void* x, const uint8_t* wg4, const uin
   return 0;
 }
 
+// --------------------------------------------------- MX (block-scaled) ---
+// Block-scaled formats ([B] module docstring: the block-scaled mode, MXFP4 /
+// MXFP8 through gemm_blockscaled with scale factors SFA / SFB; the formats
+// themselves as the OCP Microscaling specification v1.0 defines them):
+// along a row, every block of 32 values shares one E8M0 scale X = 2^(e-127)
+// (e in [0, 254]); the elements are FP8 E4M3 (max 448) or FP4 E2M1 (values
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives). FP4 codes are packed two
+// per byte, element 2i in bits 0..3 (sign in bit 3).
+//   quantisation of a block with amax = max |v|:  e = floor(log2 amax)
+//     - emax_elem + 127 (emax_elem = 8 for E4M3, 2 for E2M1; clamped to
+//     [0, 254]; e = 127 for an all-zero block), element = the value nearest
+//     to v / X on the element grid (fp32 division; ties to the even code;
+//     values beyond the largest magnitude take it).
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMxBlock = 32;
+constexpr int kMxFp8 = 0;   // element format codes (those of the MFMA operand fields)
+constexpr int kMxFp4 = 4;
+
+float fp4e2m1_to_float(int c) {
+  // sign | 2 exponent bits (bias 1) | 1 mantissa bit; exponent 0 is 0.5 * m
+  const int e = (c >> 1) & 3, m = c & 1;
+  const float mag = e == 0 ? 0.5f * m : std::ldexp(1.0f + 0.5f * m, e - 1);
+  return (c & 8) ? -mag : mag;
+}
+
+int float_to_fp4e2m1(float v) {
+  const float a = std::fabs(v);
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    const float dc = std::fabs(a - fp4e2m1_to_float(c)), db = std::fabs(a - fp4e2m1_to_float(best));
+    if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+  }
+  return (v < 0.0f && best != 0) ? (best | 8) : best;
+}
+
+int mx_scale_exp(float amax, int emax_elem) {
+  if (!(amax > 0.0f)) return 127;
+  int e2;
+  std::frexp(amax, &e2);                    // amax = f * 2^e2, f in [0.5, 1)
+  const int e = (e2 - 1) - emax_elem + 127;
+  return e < 0 ? 0 : (e > 254 ? 254 : e);
+}
+
+float e8m0_to_float(int e) { return std::ldexp(1.0f, e - 127); }
+
+// One row of `cols` values (dtype dt, or fp32 when dt == kF32) to MX codes
+// and scales; codes: E4M3 bytes [cols] or packed E2M1 [cols / 2].
+void quantize_mx_row(int dt, const void* v, int64_t base, int cols, int fmt, uint8_t* codes,
+                     uint8_t* scales) {
+  for (int b = 0; b < cols / kMxBlock; ++b) {
+    float amax = 0.0f;
+    for (int i = 0; i < kMxBlock; ++i) amax = std::fmax(amax, std::fabs(load_elem(dt, v, base + b * kMxBlock + i)));
+    const int e = mx_scale_exp(amax, fmt == kMxFp4 ? 2 : 8);
+    scales[b] = static_cast<uint8_t>(e);
+    const float X = e8m0_to_float(e);
+    for (int i = 0; i < kMxBlock; ++i) {
+      const int k = b * kMxBlock + i;
+      const float q = load_elem(dt, v, base + k) / X;
+      if (fmt == kMxFp4) {
+        const int c = float_to_fp4e2m1(q);
+        if (k % 2 == 0) codes[k / 2] = static_cast<uint8_t>(c);
+        else codes[k / 2] = static_cast<uint8_t>(codes[k / 2] | (c << 4));
+      } else {
+        codes[k] = float_to_fp8e4m3_bits(q);
+      }
+    }
+  }
+}
+
+// Decoded value k of an MX row (X * element).
+float mx_value(const uint8_t* codes, const uint8_t* scales, int fmt, int64_t k) {
+  const float X = e8m0_to_float(scales[k / kMxBlock]);
+  const float el = fmt == kMxFp4 ? fp4e2m1_to_float((codes[k >> 1] >> (4 * (k & 1))) & 0xF)
+                                 : fp8e4m3_bits_to_float(codes[k]);
+  return X * el;
+}
+
+}  // namespace
+
+extern "C" {
+
+// MX quantisation of `rows` rows of `cols` values (cols % 32 == 0): fmt 0 =
+// MXFP8 (E4M3 codes [rows, cols]), 4 = MXFP4 (packed E2M1 [rows, cols / 2]);
+// scales: E8M0 bytes [rows, cols / 32].
+int oracle_quantize_mx_rows(int dt, const void* v, int64_t rows, int cols, int fmt,
+                            uint8_t* codes, uint8_t* scales) {
+  if (!dtype_ok(dt) || rows < 0 || cols <= 0 || cols % kMxBlock || (fmt != kMxFp8 && fmt != kMxFp4)) return -1;
+  const int64_t cb = fmt == kMxFp4 ? cols / 2 : cols;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    quantize_mx_row(dt, v, r * cols, cols, fmt, codes + r * cb, scales + r * (cols / kMxBlock));
+  }
+  return 0;
+}
+
+// Decoded MX values (fp32, exact: a power of two times an element value).
+int oracle_mx_decode(const uint8_t* codes, const uint8_t* scales, int64_t rows, int cols, int fmt,
+                     float* out) {
+  if (rows < 0 || cols <= 0 || cols % kMxBlock || (fmt != kMxFp8 && fmt != kMxFp4)) return -1;
+  const int64_t cb = fmt == kMxFp4 ? cols / 2 : cols;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int k = 0; k < cols; ++k) {
+      out[r * cols + k] = mx_value(codes + r * cb, scales + r * (cols / kMxBlock), fmt, k);
+    }
+  }
+  return 0;
+}
+
+// The forward with MX experts: MXFP4 weights (packed E2M1 [E, D, H/2] gate /
+// up, [E, H, D/2] down, E8M0 scales [E, D, H/32] / [E, H, D/32]) against
+// MXFP8 activations: x quantised per token row, h per routed pair. Per pair:
+//   g_j  = fp32 fma chain over h ascending of X(x) x(h) * X(wg) wg(h)  (each
+//          product of two decoded values is exact), u_j likewise
+//   h_j  = R(SiLU(g_j) * u_j)
+//   eo_c = R(fp32 fma chain over j of decoded h (MXFP8) * decoded Wd)
+// and y as oracle_moe_forward.
+int oracle_moe_forward_mx(int dt, const void* x, const uint8_t* wg, const uint8_t* wu,
+                          const uint8_t* wd, const uint8_t* sg, const uint8_t* su,
+                          const uint8_t* sd, const int32_t* ids, const float* w, int T, int H,
+                          int D, int E, int K, const int32_t* tokens, int n_tokens, float* y,
+                          float* h_pairs, float* eo_pairs) {
+  if (!dtype_ok(dt) || T < 0 || H <= 0 || D <= 0 || E <= 0 || K <= 0 || H % kMxBlock || D % kMxBlock) return -1;
+  if (!tokens && n_tokens != T) return -1;
+  for (int i = 0; i < n_tokens; ++i) {
+    const int t = tokens ? tokens[i] : i;
+    if (t < 0 || t >= T) return -1;
+    for (int k = 0; k < K; ++k) {
+      if (ids[static_cast<int64_t>(t) * K + k] >= E) return -1;
+    }
+  }
+#pragma omp parallel
+  {
+    std::vector<uint8_t> xc(H), xs(H / kMxBlock), hc(D), hs(D / kMxBlock);
+    std::vector<float> xv(H), hv(D), hbuf(D), eo(H), acc(H);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < n_tokens; ++i) {
+      const int t = tokens ? tokens[i] : i;
+      quantize_mx_row(dt, x, static_cast<int64_t>(t) * H, H, kMxFp8, xc.data(), xs.data());
+      for (int c = 0; c < H; ++c) xv[c] = mx_value(xc.data(), xs.data(), kMxFp8, c);
+      for (int c = 0; c < H; ++c) acc[c] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int64_t slot = static_cast<int64_t>(t) * K + k;
+        const int64_t out_slot = static_cast<int64_t>(i) * K + k;
+        const int e = ids[slot];
+        if (e < 0) {
+          if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = 0.0f;
+          if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = 0.0f;
+          continue;
+        }
+        for (int j = 0; j < D; ++j) {
+          const int64_t row = static_cast<int64_t>(e) * D + j;
+          const uint8_t *gc = wg + row * (H / 2), *uc = wu + row * (H / 2);
+          const uint8_t *gs = sg + row * (H / kMxBlock), *us = su + row * (H / kMxBlock);
+          float g = 0.0f, u = 0.0f;
+          for (int c = 0; c < H; ++c) {
+            g = std::fma(xv[c], mx_value(gc, gs, kMxFp4, c), g);
+            u = std::fma(xv[c], mx_value(uc, us, kMxFp4, c), u);
+          }
+          hbuf[j] = round_to(dt, silu(g) * u);
+        }
+        quantize_mx_row(kF32, hbuf.data(), 0, D, kMxFp8, hc.data(), hs.data());
+        for (int j = 0; j < D; ++j) hv[j] = mx_value(hc.data(), hs.data(), kMxFp8, j);
+        for (int c = 0; c < H; ++c) {
+          const int64_t row = static_cast<int64_t>(e) * H + c;
+          const uint8_t *dc = wd + row * (D / 2), *ds = sd + row * (D / kMxBlock);
+          float o = 0.0f;
+          for (int j = 0; j < D; ++j) o = std::fma(hv[j], mx_value(dc, ds, kMxFp4, j), o);
+          eo[c] = round_to(dt, o);
+        }
+        const float wk = w[slot];
+        for (int c = 0; c < H; ++c) acc[c] = std::fma(wk, eo[c], acc[c]);
+        if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = hbuf[j];
+        if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = eo[c];
+      }
+      for (int c = 0; c < H; ++c) y[static_cast<int64_t>(i) * H + c] = acc[c];
+    }
+  }
+  return 0;
+}
+
 // -------------------------------------------------------- weighted reduce --
 // moe_reduce_fused ([C] sections 1-2) and its scaled variants ([C] section 1
 // and the commit note on the scaled variants: with_x_sf multiplies once per
