@@ -313,6 +313,51 @@ moe_status moe_routed_forward_w4a8(const void* x, const uint8_t* w_gate, const u
                                    int dtype, void* workspace, size_t workspace_bytes, void* y,
                                    void* stream);
 
+/* Block-scaled (MX) experts ([B] module docstring: the block-scaled mode,
+ * gemm_blockscaled with per-block scale factors of both operands; formats
+ * as the OCP Microscaling specification v1.0 defines them): along a row,
+ * every block of 32 values shares one E8M0 scale byte e (X = 2^(e-127));
+ * elements are FP8 E4M3 (MOE_MX_FP8: one byte each) or FP4 E2M1 (MOE_MX_FP4:
+ * two per byte, element 2i in bits 0..3).
+ *
+ * moe_quantize_mx_rows: per 32-block with amax = max |v|:
+ *   e = floor(log2 amax) - emax_elem + 127 (emax_elem 8 for E4M3, 2 for
+ *       E2M1; clamped to [0, 254]; 127 for an all-zero block),
+ *   element = the grid value nearest to v / X (fp32 division, ties to the
+ *       even code, saturating at the largest magnitude).
+ *   v [rows, cols] of dtype (MOE_F16, MOE_BF16, MOE_F32), cols % 32 == 0;
+ *   codes [rows, cols] (FP8) or [rows, cols/2] (FP4), 16-byte aligned;
+ *   scales uint8 [rows, cols/32].
+ *
+ * moe_expert_gate_up_mx / moe_expert_down_mx: MXFP4 weights w_gate, w_up
+ * [E, D, H/2] and w_down [E, H, D/2] with scales [E, D, H/32] / [E, H, D/32]
+ * against MXFP8 activations xq [T, H] with xs [T, H/32] (token order) and
+ * hq [P, D] with hs [P, D/32] (sorted order); every dot product is
+ * sum_k (X_a a_k)(X_w w_k), accumulated in fp32 by the scaled MFMA:
+ *   h = R(SiLU(g) * u),  expert_out = R(hq . Wd).
+ * dtype (of h / expert_out): MOE_F16 or MOE_BF16; D % 256 == 0 besides the
+ * 16-bit calls' rules. moe_routed_forward_mx: x -> MXFP8; gate/up; h ->
+ * MXFP8 per sorted row; down; moe_reduce_fused. Workspace
+ * (moe_forward_mx_workspace_bytes, 256-byte aligned): h, expert_out as
+ * moe_routed_forward's, then xq, xs, hq, hs. Errors as the 16-bit calls. */
+#define MOE_MX_FP8 0
+#define MOE_MX_FP4 4
+moe_status moe_quantize_mx_rows(const void* v, int64_t rows, int cols, int dtype, int fmt,
+                                uint8_t* codes, uint8_t* scales, void* stream);
+moe_status moe_expert_gate_up_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* w_gate,
+                                 const uint8_t* w_up, const uint8_t* s_gate, const uint8_t* s_up,
+                                 const moe_tables* tables, int H, int D, int dtype, void* h,
+                                 void* stream);
+moe_status moe_expert_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w_down,
+                              const uint8_t* s_down, const moe_tables* tables, int H, int D,
+                              int dtype, void* expert_out, void* stream);
+size_t moe_forward_mx_workspace_bytes(int T, int K, int H, int D, int dtype);
+moe_status moe_routed_forward_mx(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                 const uint8_t* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                 const uint8_t* s_down, const moe_tables* tables, int H, int D,
+                                 int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                 void* stream);
+
 /* Step 3: top-k weighted reduce back to token order ([C] sections 1-2):
  *   y[t, :] = R_out( sum over k = 0..K-1 ascending with pos[t,k] >= 0 of
  *                    w[t,k] * expert_out[pos[t,k], :] )

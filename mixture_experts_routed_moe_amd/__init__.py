@@ -26,7 +26,11 @@ __all__ = ["MoeError", "MoeTables", "FP8Weights", "default_block_m", "moe_gate",
            "moe_expert_down", "moe_routed_forward", "moe_reduce_fused", "forward_workspace",
            "W4Weights", "quantize_int8_rows", "quantize_int4_rows", "w4a8_gemm",
            "moe_expert_gate_up_w4a8", "moe_expert_down_w4a8", "forward_w4a8_workspace",
-           "moe_routed_forward_w4a8"]
+           "moe_routed_forward_w4a8", "MX_FP8", "MX_FP4", "MXWeights", "quantize_mx_rows",
+           "quantize_mx_weights", "moe_expert_gate_up_mx", "moe_expert_down_mx",
+           "forward_mx_workspace", "moe_routed_forward_mx"]
+
+MX_FP8, MX_FP4 = 0, 4
 
 _DTYPE_CODE = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
 # The reduce also reads and writes OCP FP8 E4M3 ("fn").
@@ -519,6 +523,161 @@ def moe_routed_forward_w4a8(x, w_gate, w_up, w_down, tables, y=None, workspace=N
                                         _ptr(w_up.scales), _ptr(w_down.scales), tables.ref, H, D,
                                         _DTYPE_CODE[x.dtype], _ptr(workspace), workspace.numel(),
                                         _ptr(y), _stream(x.device)))
+    return y
+
+
+class MXWeights:
+    """Stacked expert weights in MXFP4: `packed` uint8 [E, N, Kd/2] (E2M1
+    codes, element 2i in the low nibble) and E8M0 block scales `scales`
+    uint8 [E, N, Kd/32]. `shape` is the logical [E, N, Kd]."""
+
+    def __init__(self, packed, scales):
+        _check_tensor(packed, "packed", torch.uint8, 3)
+        _check_tensor(scales, "scales", torch.uint8, 3, packed.device)
+        E, N, half = packed.shape
+        _require(tuple(scales.shape) == (E, N, half * 2 // 32), MOE_ERR_SHAPE,
+                 "scales must be [E, N, Kd/32] = %s" % ((E, N, half * 2 // 32),))
+        self.packed = packed
+        self.scales = scales
+
+    @property
+    def shape(self):
+        E, N, half = self.packed.shape
+        return torch.Size((E, N, 2 * half))
+
+    def dim(self):
+        return 3
+
+
+def quantize_mx_rows(v, fmt=MX_FP8, codes=None, scales=None):
+    """moe_quantize_mx_rows on v [rows, cols] (fp16 / bf16 / fp32, cols a
+    multiple of 32): MX codes (MX_FP8: [rows, cols]; MX_FP4: packed [rows,
+    cols/2]) and E8M0 scales [rows, cols/32]. Returns (codes, scales)."""
+    _check_tensor(v, "v", None, 2)
+    _require(v.dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "v must be float16, bfloat16 or float32")
+    rows, cols = v.shape
+    cshape = (rows, cols) if fmt == MX_FP8 else (rows, cols // 2)
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=v.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=v.device)
+    _check_tensor(codes, "codes", torch.uint8, 2, v.device)
+    _check_tensor(scales, "scales", torch.uint8, 2, v.device)
+    _require(tuple(codes.shape) == cshape and tuple(scales.shape) == (rows, cols // 32),
+             MOE_ERR_SHAPE, "codes must be %s and scales [%d, %d]" % (cshape, rows, cols // 32))
+    check(lib().moe_quantize_mx_rows(_ptr(v), rows, cols, _DTYPE_CODE[v.dtype], fmt, _ptr(codes),
+                                      _ptr(scales), _stream(v.device)))
+    return codes, scales
+
+
+def quantize_mx_weights(w):
+    """MXFP4 quantisation of stacked weights w [E, N, Kd]. Returns MXWeights."""
+    _check_tensor(w, "w", None, 3)
+    E, N, Kd = w.shape
+    codes, scales = quantize_mx_rows(w.view(E * N, Kd), MX_FP4)
+    return MXWeights(codes.view(E, N, Kd // 2), scales.view(E, N, Kd // 32))
+
+
+def _mx_shapes(act, scales, w_a, w_b, w_down, tables, gate_up, dtype):
+    _require(dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "MX experts produce float16 or bfloat16")
+    _check_tensor(act, "activations", torch.uint8, 2, tables.device)
+    _check_tensor(scales, "activation scales", torch.uint8, 2, tables.device)
+    for n, w in (("w_a", w_a), ("w_b", w_b), ("w_down", w_down)):
+        if w is not None:
+            _require(isinstance(w, MXWeights), MOE_ERR_DTYPE, "%s must be MXWeights" % n)
+            _require(w.packed.device == tables.device, MOE_ERR_SHAPE, "%s is on another device" % n)
+    E = tables.E
+    rows, kd = act.shape
+    _require(tuple(scales.shape) == (rows, kd // 32), MOE_ERR_SHAPE, "activation scales must be [rows, kd/32]")
+    if gate_up:
+        _require(rows == tables.T, MOE_ERR_SHAPE, "xq has %d rows, tables %d tokens" % (rows, tables.T))
+        H = kd
+        _require(w_a.shape[0] == E and w_a.shape[2] == H, MOE_ERR_SHAPE,
+                 "w_gate must be [E=%d, D, H=%d] (got %s)" % (E, H, tuple(w_a.shape)))
+        D = w_a.shape[1]
+        _require(tuple(w_b.shape) == (E, D, H), MOE_ERR_SHAPE, "w_up must be [%d, %d, %d]" % (E, D, H))
+        return H, D
+    _require(rows == tables.T * tables.K, MOE_ERR_SHAPE, "hq must have T*K rows")
+    D = kd
+    _require(w_a.shape[0] == E and w_a.shape[2] == D, MOE_ERR_SHAPE,
+             "w_down must be [E=%d, H, D=%d] (got %s)" % (E, D, tuple(w_a.shape)))
+    return w_a.shape[1], D
+
+
+def moe_expert_gate_up_mx(xq, xs, w_gate, w_up, tables, dtype=torch.bfloat16, h=None):
+    """Step 2a with MX experts: MXFP8 xq [T, H] (scales xs [T, H/32])
+    against MXWeights [E, D, H]; h [T*K, D] of dtype."""
+    H, D = _mx_shapes(xq, xs, w_gate, w_up, None, tables, True, dtype)
+    if h is None:
+        h = torch.empty(tables.T * tables.K, D, dtype=dtype, device=xq.device)
+    _check_tensor(h, "h", dtype, 2, tables.device)
+    check(lib().moe_expert_gate_up_mx(_ptr(xq), _ptr(xs), _ptr(w_gate.packed), _ptr(w_up.packed),
+                                      _ptr(w_gate.scales), _ptr(w_up.scales), tables.ref, H, D,
+                                      _DTYPE_CODE[dtype], _ptr(h), _stream(xq.device)))
+    return h
+
+
+def moe_expert_down_mx(hq, hs, w_down, tables, dtype=torch.bfloat16, expert_out=None):
+    """Step 2b with MX experts: MXFP8 hq [T*K, D] (scales hs [T*K, D/32])
+    against MXWeights [E, H, D]; expert_out [T*K, H] of dtype."""
+    H, D = _mx_shapes(hq, hs, w_down, None, None, tables, False, dtype)
+    if expert_out is None:
+        expert_out = torch.empty(tables.T * tables.K, H, dtype=dtype, device=hq.device)
+    _check_tensor(expert_out, "expert_out", dtype, 2, tables.device)
+    check(lib().moe_expert_down_mx(_ptr(hq), _ptr(hs), _ptr(w_down.packed), _ptr(w_down.scales),
+                                   tables.ref, H, D, _DTYPE_CODE[dtype], _ptr(expert_out),
+                                   _stream(hq.device)))
+    return expert_out
+
+
+def forward_mx_workspace(tables, H, D, dtype):
+    """A workspace for moe_routed_forward_mx and views of its buffers:
+    (ws, h, expert_out, xq, xs, hq, hs)."""
+    code = _DTYPE_CODE[dtype]
+    nbytes = lib().moe_forward_mx_workspace_bytes(tables.T, tables.K, H, D, code)
+    _require(nbytes > 0, MOE_ERR_SHAPE, "invalid workspace sizes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=tables.device)
+    base = lib().moe_forward_workspace_bytes(tables.T, tables.K, H, D, code)
+    off = lib().moe_forward_workspace_expert_out_offset(tables.T, tables.K, H, D, code)
+    T, P = tables.T, tables.T * tables.K
+    esz = torch.empty((), dtype=dtype).element_size()
+    up = lambda v: (v + 255) // 256 * 256
+    h = ws[:P * D * esz].view(dtype).view(P, D)
+    eo = ws[off:off + P * H * esz].view(dtype).view(P, H)
+    o_xq = base
+    o_xs = o_xq + up(T * H)
+    o_hq = o_xs + up(T * (H // 32))
+    o_hs = o_hq + up(P * D)
+    xq = ws[o_xq:o_xq + T * H].view(T, H)
+    xs = ws[o_xs:o_xs + T * (H // 32)].view(T, H // 32)
+    hq = ws[o_hq:o_hq + P * D].view(P, D)
+    hs = ws[o_hs:o_hs + P * (D // 32)].view(P, D // 32)
+    return ws, h, eo, xq, xs, hq, hs
+
+
+def moe_routed_forward_mx(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
+    """Steps 2-3 with MX experts (MXWeights; x 16-bit, quantised to MXFP8
+    per token inside): y [T, H] of x.dtype."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    _require(x.dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "MX experts take float16 or bfloat16 activations")
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _require(isinstance(w, MXWeights), MOE_ERR_DTYPE, "%s must be MXWeights" % n)
+        _require(w.packed.device == tables.device, MOE_ERR_SHAPE, "%s is on another device" % n)
+    H, D = _expert_shapes(x, w_gate, w_up, w_down, tables, True)
+    if workspace is None:
+        workspace = forward_mx_workspace(tables, H, D, x.dtype)[0]
+    _check_tensor(workspace, "workspace", torch.uint8, 1, tables.device)
+    if y is None:
+        y = torch.empty(tables.T, H, dtype=x.dtype, device=x.device)
+    _check_tensor(y, "y", x.dtype, 2, tables.device)
+    _require(tuple(y.shape) == (tables.T, H), MOE_ERR_SHAPE, "y must be [T, H]")
+    check(lib().moe_routed_forward_mx(_ptr(x), _ptr(w_gate.packed), _ptr(w_up.packed),
+                                      _ptr(w_down.packed), _ptr(w_gate.scales),
+                                      _ptr(w_up.scales), _ptr(w_down.scales), tables.ref, H, D,
+                                      _DTYPE_CODE[x.dtype], _ptr(workspace), workspace.numel(),
+                                      _ptr(y), _stream(x.device)))
     return y
 
 

@@ -102,6 +102,17 @@ def lib():
         L.moe_routed_forward_w4a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp,
                                               sz, vp, vp]
         L.moe_routed_forward_w4a8.restype = i32
+        L.moe_quantize_mx_rows.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
+        L.moe_quantize_mx_rows.restype = i32
+        L.moe_expert_gate_up_mx.argtypes = [vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_gate_up_mx.restype = i32
+        L.moe_expert_down_mx.argtypes = [vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_down_mx.restype = i32
+        L.moe_forward_mx_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_forward_mx_workspace_bytes.restype = sz
+        L.moe_routed_forward_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp, sz,
+                                            vp, vp]
+        L.moe_routed_forward_mx.restype = i32
         _lib = L
     return _lib
 

@@ -152,6 +152,31 @@ W4Layout w4_layout(int T, int K, int H, int D, size_t base) {
   return L;
 }
 
+moe_status check_mx_shapes(const moe_tables* t, int H, int D, int dtype) {
+  moe_status s = check_expert_shapes(t, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (!is_16bit(dtype)) return fail(MOE_ERR_DTYPE, "MX experts take MOE_F16 or MOE_BF16 activations");
+  if (D % 256 != 0) return fail(MOE_ERR_SHAPE, "MX experts need D a multiple of 256 (got %d)", D);
+  return MOE_OK;
+}
+
+// Workspace of the MX forward: the 16-bit forward's h and expert_out, then
+// xq [T, H] E4M3, xs [T, H/32] E8M0, hq [P, D], hs [P, D/32], each 256-aligned.
+struct MxLayout {
+  size_t xq, xs, hq, hs, total;
+};
+
+MxLayout mx_layout(int T, int K, int H, int D, size_t base) {
+  const size_t P = static_cast<size_t>(T) * K;
+  MxLayout L;
+  L.xq = base;
+  L.xs = L.xq + align_up(static_cast<size_t>(T) * H);
+  L.hq = L.xs + align_up(static_cast<size_t>(T) * (H / 32));
+  L.hs = L.hq + align_up(P * D);
+  L.total = L.hs + align_up(P * (D / 32));
+  return L;
+}
+
 size_t ws_h_bytes(int T, int K, int D, int dtype) {
   return static_cast<size_t>(T) * K * D * dtype_bytes(dtype);
 }
@@ -503,6 +528,103 @@ moe_status moe_routed_forward_w4a8(const void* x, const uint8_t* w_gate, const u
   err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
                            nullptr, T, K, H, dtype, dtype, y, st);
   return hip_status(err, "moe_routed_forward_w4a8 reduce launch");
+}
+
+moe_status moe_quantize_mx_rows(const void* v, int64_t rows, int cols, int dtype, int fmt,
+                                uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!v || !codes || !scales) return fail(MOE_ERR_NULL, "v, codes and scales must not be NULL");
+  if (rows < 0 || cols <= 0 || cols % 32 != 0) {
+    return fail(MOE_ERR_SHAPE, "rows must be >= 0 and cols a positive multiple of 32");
+  }
+  if (rows > (int64_t{1} << 33)) return fail(MOE_ERR_SHAPE, "too many rows for one launch");
+  if (!is_float(dtype)) return fail(MOE_ERR_DTYPE, "dtype must be MOE_F16, MOE_BF16 or MOE_F32");
+  if (fmt != MOE_MX_FP8 && fmt != MOE_MX_FP4) {
+    return fail(MOE_ERR_DTYPE, "fmt must be MOE_MX_FP8 or MOE_MX_FP4 (got %d)", fmt);
+  }
+  if (reinterpret_cast<uintptr_t>(codes) % 16 != 0) {
+    return fail(MOE_ERR_SHAPE, "codes must be 16-byte aligned");
+  }
+  if (rows == 0) return ok();
+  return hip_status(moe::launch_quantize_mx_rows(v, rows, cols, dtype, fmt, codes, scales,
+                                                 static_cast<hipStream_t>(stream)),
+                    "moe_quantize_mx_rows launch");
+}
+
+moe_status moe_expert_gate_up_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* w_gate,
+                                 const uint8_t* w_up, const uint8_t* s_gate, const uint8_t* s_up,
+                                 const moe_tables* tables, int H, int D, int dtype, void* h,
+                                 void* stream) {
+  if (!xq || !xs || !w_gate || !w_up || !s_gate || !s_up || !h) {
+    return fail(MOE_ERR_NULL, "xq, xs, w_gate, w_up, s_gate, s_up and h must not be NULL");
+  }
+  moe_status s = check_mx_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  moe::MxGemmProblem p{xq, xs, w_gate, w_up, s_gate, s_up, h, D, H, dtype};
+  return hip_status(moe::launch_gate_up_mx(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_gate_up_mx launch");
+}
+
+moe_status moe_expert_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w_down,
+                              const uint8_t* s_down, const moe_tables* tables, int H, int D,
+                              int dtype, void* expert_out, void* stream) {
+  if (!hq || !hs || !w_down || !s_down || !expert_out) {
+    return fail(MOE_ERR_NULL, "hq, hs, w_down, s_down and expert_out must not be NULL");
+  }
+  moe_status s = check_mx_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  moe::MxGemmProblem p{hq, hs, w_down, nullptr, s_down, nullptr, expert_out, H, D, dtype};
+  return hip_status(moe::launch_down_mx(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_down_mx launch");
+}
+
+size_t moe_forward_mx_workspace_bytes(int T, int K, int H, int D, int dtype) {
+  const size_t base = moe_forward_workspace_bytes(T, K, H, D, dtype);
+  if (base == 0) return 0;
+  return mx_layout(T, K, H, D, base).total;
+}
+
+moe_status moe_routed_forward_mx(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                 const uint8_t* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                 const uint8_t* s_down, const moe_tables* tables, int H, int D,
+                                 int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                 void* stream) {
+  if (!x || !w_gate || !w_up || !w_down || !s_gate || !s_up || !s_down || !workspace || !y) {
+    return fail(MOE_ERR_NULL,
+                "x, the weights, their scales, workspace and y must not be NULL");
+  }
+  moe_status s = check_mx_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  const size_t need = moe_forward_mx_workspace_bytes(tables->T, tables->K, H, D, dtype);
+  if (workspace_bytes < need) {
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) {
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const int T = tables->T, K = tables->K;
+  const int64_t P = static_cast<int64_t>(T) * K;
+  char* ws = static_cast<char*>(workspace);
+  const MxLayout L = mx_layout(T, K, H, D, moe_forward_workspace_bytes(T, K, H, D, dtype));
+  void* hbuf = ws;
+  void* eo = ws + moe_forward_workspace_expert_out_offset(T, K, H, D, dtype);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(ws + L.xs);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+  uint8_t* hs = reinterpret_cast<uint8_t*>(ws + L.hs);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = moe::launch_quantize_mx_rows(x, T, H, dtype, MOE_MX_FP8, xq, xs, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_mx x quantisation launch");
+  moe::MxGemmProblem up{xq, xs, w_gate, w_up, s_gate, s_up, hbuf, D, H, dtype};
+  err = moe::launch_gate_up_mx(up, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_mx gate/up launch");
+  err = moe::launch_quantize_mx_rows(hbuf, P, D, dtype, MOE_MX_FP8, hq, hs, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_mx h quantisation launch");
+  moe::MxGemmProblem down{hq, hs, w_down, nullptr, s_down, nullptr, eo, H, D, dtype};
+  err = moe::launch_down_mx(down, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_mx down launch");
+  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
+                           nullptr, T, K, H, dtype, dtype, y, st);
+  return hip_status(err, "moe_routed_forward_mx reduce launch");
 }
 
 moe_status moe_reduce_fused_scaled(const void* expert_out, int64_t rows,

@@ -54,6 +54,25 @@ hipError_t launch_quantize_int8_rows(const void* a, int64_t rows, int cols, int 
                                      float* scales, hipStream_t stream);
 hipError_t launch_quantize_int4_rows(const void* w, int64_t rows, int cols, int dtype,
                                      uint8_t* packed, float* scales, hipStream_t stream);
+// MX: MXFP8 activations (E4M3 codes a, E8M0 block scales as) against MXFP4
+// weights (packed E2M1 b0 / b1, E8M0 block scales s0 / s1); output c in
+// dtype (kF16 / kBF16).
+struct MxGemmProblem {
+  const uint8_t* a;      // gate/up: xq [T, kd]; down: hq [P, kd]
+  const uint8_t* as;     // [rows, kd/32]
+  const uint8_t* b0;     // [E, n, kd/2]
+  const uint8_t* b1;
+  const uint8_t* s0;     // [E, n, kd/32]
+  const uint8_t* s1;
+  void* c;
+  int n;
+  int kd;
+  int dtype;
+};
+hipError_t launch_gate_up_mx(const MxGemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_down_mx(const MxGemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_quantize_mx_rows(const void* v, int64_t rows, int cols, int dtype, int fmt,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_gate_up_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down_f32(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 
