@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pmc_grouped_gemm_gate_up_deepseek_decode.md")
 GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", f)
@@ -86,19 +87,22 @@ def workload_numbers(d, tables_sizes, weights="16bit"):
     copies of x and h (and their scales), written once and read once."""
     T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
     b = d["x"].element_size()
-    wb = {"16bit": b, "fp8": 1, "w4a8": 0.5}[weights]
-    sc = 0 if weights == "16bit" else 4   # scale bytes per weight row
+    wb = {"16bit": b, "fp8": 1, "w4a8": 0.5, "mx": 0.5 + 1 / 32}[weights]
+    sc = 4 if weights in ("fp8", "w4a8") else 0   # scale bytes per weight row
     n_valid = int(tables_sizes.sum())
     e_active = int((tables_sizes > 0).sum())
     P = T * K
     w_gate_up = int(e_active * 2 * D * (H * wb + sc))
     w_down = int(e_active * H * (D * wb + sc))
     out = dict(n_valid=n_valid, e_active=e_active)
-    if weights == "w4a8":
-        out["quant_x_bytes"] = T * H * b + T * H + T * 4
-        out["gate_up_bytes"] = w_gate_up + T * H + T * 4 + n_valid * D * b
-        out["quant_h_bytes"] = P * D * b + P * D + P * 4
-        out["down_bytes"] = w_down + n_valid * D + n_valid * 4 + n_valid * H * b
+    if weights in ("w4a8", "mx"):
+        # int8 + a 4-byte scale per row, or E4M3 + an E8M0 byte per 32 values
+        ab = 1 + 1 / 32 if weights == "mx" else 1
+        rs = 0 if weights == "mx" else 4
+        out["quant_x_bytes"] = int(T * H * b + T * H * ab + T * rs)
+        out["gate_up_bytes"] = int(w_gate_up + T * H * ab + T * rs + n_valid * D * b)
+        out["quant_h_bytes"] = int(P * D * b + P * D * ab + P * rs)
+        out["down_bytes"] = int(w_down + n_valid * D * ab + n_valid * rs + n_valid * H * b)
     else:
         out["gate_up_bytes"] = w_gate_up + T * H * b + n_valid * D * b
         out["down_bytes"] = w_down + n_valid * D * b + n_valid * H * b
@@ -128,7 +132,8 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit"):
     t_gen = time.time() - t_gen
     quant_ms = None
     if weights != "16bit":
-        qfn = mr.quantize_fp8_rows if weights == "fp8" else mr.quantize_int4_rows
+        qfn = {"fp8": mr.quantize_fp8_rows, "w4a8": mr.quantize_int4_rows,
+               "mx": mr.quantize_mx_weights}[weights]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
         q = [qfn(d[n]) for n in ("w_gate", "w_up", "w_down")]
@@ -143,6 +148,9 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit"):
     tables = mr.MoeTables(T, K, E, block_m, dev)
     if weights == "w4a8":
         ws, h, eo, xq, sx, hq, sh = mr.forward_w4a8_workspace(tables, H, D, x.dtype)
+        names = ["dispatch", "quant_x", "gate_up", "quant_h", "down", "reduce"]
+    elif weights == "mx":
+        ws, h, eo, xq, sx, hq, sh = mr.forward_mx_workspace(tables, H, D, x.dtype)
         names = ["dispatch", "quant_x", "gate_up", "quant_h", "down", "reduce"]
     else:
         ws, h, eo = mr.forward_workspace(tables, H, D, x.dtype)
@@ -163,6 +171,15 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit"):
             mr.quantize_int8_rows(h, q=hq, scales=sh)
             ev[4].record()
             mr.moe_expert_down_w4a8(hq, sh, wd, tables, x.dtype, expert_out=eo)
+            ev[5].record()
+        elif weights == "mx":
+            mr.quantize_mx_rows(x, mr.MX_FP8, codes=xq, scales=sx)
+            ev[2].record()
+            mr.moe_expert_gate_up_mx(xq, sx, wg, wu, tables, x.dtype, h=h)
+            ev[3].record()
+            mr.quantize_mx_rows(h, mr.MX_FP8, codes=hq, scales=sh)
+            ev[4].record()
+            mr.moe_expert_down_mx(hq, sh, wd, tables, x.dtype, expert_out=eo)
             ev[5].record()
         else:
             if weights == "fp8":
@@ -210,8 +227,10 @@ def summarize(r):
     for n, key in (("gate_up", "flops_gate_up"), ("down", "flops_down")):
         kernels[n]["TFLOP_s" if r.get("weights") != "w4a8" else "TOP_s"] = \
             round(nums[key] / (per[n] * 1e-3) / 1e12, 2)
-    # W4A8 runs int8 MFMA (5.0 POP/s dense); the others bf16 / fp16 MFMA
-    peak = MFMA_INT8_PEAK_TOPS if r.get("weights") == "w4a8" else MFMA_BF16_PEAK_TFLOPS
+    # W4A8 runs int8 MFMA (5.0 POP/s dense), MX the FP8 x FP4 scaled MFMA
+    # (5.0 PFLOP/s at the FP8 rate); the others bf16 / fp16 MFMA
+    peak = {"w4a8": MFMA_INT8_PEAK_TOPS, "mx": MFMA_FP8_PEAK_TFLOPS}.get(r.get("weights"),
+                                                                      MFMA_BF16_PEAK_TFLOPS)
     tflops = nums["flops"] / (ms * 1e-3) / 1e12
     hbm = gbs(nums["b_min"], ms)
     t_roof_ms = max(nums["b_min"] / (HBM_PEAK_GBS * 1e9), nums["flops"] / (peak * 1e12)) * 1e3
@@ -531,6 +550,18 @@ def main():
                               "scales; int8 activations, per-row scales)")
             w4["T%d" % S.CONFIGS[ci]["T"]] = s4
         extras["w4a8"] = w4
+        mx = {}
+        for ci in (2, 3):
+            rm = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev, weights="mx")
+            rm.pop("d")
+            rm.pop("tables")
+            torch.cuda.empty_cache()
+            sm = summarize(rm)
+            sm["quantize_ms"] = round(rm["quant_ms"], 3)
+            sm["workload"] = (S.CONFIGS[ci]["name"] + " with MX experts (MXFP4 weights, MXFP8 "
+                              "activations, E8M0 scales per 32 values)")
+            mx["T%d" % S.CONFIGS[ci]["T"]] = sm
+        extras["mx"] = mx
         extras["w4a8_gemm"] = time_w4a8_gemm(args.steps, args.warmup, dev)
         torch.cuda.empty_cache()
         print("# %s" % json.dumps(extras), file=sys.stderr, flush=True)
@@ -567,6 +598,7 @@ def main():
         "fp8_weights": extras.get("fp8_weights"),
         "w4a8": extras.get("w4a8"),
         "w4a8_gemm": extras.get("w4a8_gemm"),
+        "mx": extras.get("mx"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
