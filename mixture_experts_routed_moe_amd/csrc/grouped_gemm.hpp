@@ -73,6 +73,12 @@ constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
 #ifndef MOE_W8_RG1_STAGES
 #define MOE_W8_RG1_STAGES 4
 #endif
+#ifndef MOE_RG_ROT
+#define MOE_RG_ROT 1
+#endif
+#ifndef MOE_RG_EARLY_PREFETCH
+#define MOE_RG_EARLY_PREFETCH 0
+#endif
 #ifndef MOE_W8_WIDE_STAGES
 #define MOE_W8_WIDE_STAGES 4
 #endif
@@ -288,6 +294,9 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
   auto step = [&](int c, auto U, bool prefetch, bool stage) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
     if (prefetch) load_chunk(c + S - 1, (u + S - 1) % S);
+#if MOE_RG_EARLY_PREFETCH
+    __builtin_amdgcn_sched_barrier(0);   // issue the prefetch before the MFMAs
+#endif
     constexpr int buf = u & 1;   // S is even, so c & 1 == u & 1
 #pragma unroll
     for (int t = 0; t < CK / 16; ++t) {
@@ -380,7 +389,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   weight_rows<GATEUP, W8, CK>(g, e, nt, wave, lr, lh, col0, bptr, scale);
 
   const int nchunks = g.kd / CK;
-  const int rot = 0;   // start of the reduction walk (chunk index rotation)
+  // Start of the reduction walk (a rotation of the chunk order): 16-bit
+  // weights start each workgroup at chunk (MOE_RG_ROT * tile) mod nchunks,
+  // so the workgroups streaming at one time touch different columns of
+  // their weight rows (rows 4 KB apart otherwise load the same columns
+  // together); FP8 weights walk from chunk 0.
+  const int rot = W8 ? 0 : static_cast<int>((static_cast<int64_t>(natural) * MOE_RG_ROT) % nchunks);
   constexpr int kASeg = CK / 8;             // 16-byte segments of an A row chunk
   constexpr int kARows = 256 / kASeg;       // A rows per pass of the threads
   constexpr int kSub = 32 / kARows;
