@@ -73,6 +73,9 @@ constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
 #ifndef MOE_W8_RG1_STAGES
 #define MOE_W8_RG1_STAGES 4
 #endif
+#ifndef MOE_WIDE_ROT
+#define MOE_WIDE_ROT 1
+#endif
 #ifndef MOE_RG_ROT
 #define MOE_RG_ROT 1
 #endif
@@ -488,8 +491,8 @@ template <int DT, int NA, bool GATEUP, int S, int NAMAX, bool W8>
 __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
                                           const uint16_t* const* a_src,
                                           const uint8_t* const* bptr, const float* scale,
-                                          int nchunks, int wave, int lane, int lr, int lh,
-                                          int64_t out_row0, int rows, int col0) {
+                                          int nchunks, int rot, int wave, int lane, int lr,
+                                          int lh, int64_t out_row0, int rows, int col0) {
   constexpr int kStage = NAMAX * 4 * kAGroupElems;
   constexpr int kB = 2 * BChunk<DT, W8>::kVec;   // weight loads per chunk per wave
   constexpr int kOps = NA + kB;                   // vector memory ops per chunk per wave
@@ -503,7 +506,9 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
   u32x4 aring[S][NA];
 
   auto load_chunk = [&](int c, int slot) __attribute__((always_inline)) {
-    const int64_t off = static_cast<int64_t>(c) * kChunkK;
+    int cc = c + rot;
+    if (cc >= nchunks) cc -= nchunks;
+    const int64_t off = static_cast<int64_t>(cc) * kChunkK;
 #pragma unroll
     for (int q = 0; q < NA; ++q) aring[slot][q] = load16(a_src[q] + off);
     bring[slot].load(bptr, off);
@@ -641,6 +646,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
   const int lh = lane >> 5;
   const int64_t kd = g.kd;
   const int nchunks = g.kd / kChunkK;
+  // Start of the reduction walk, as in grouped_gemm_kernel but by column
+  // tile: the row blocks of one expert that share a weight tile still walk
+  // it together (and share it in L2), different tiles start apart.
+  const int rot = MOE_WIDE_ROT && !W8 ? nt % nchunks : 0;
 
   int col0;
   const uint8_t* bptr[2];
@@ -672,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
     static_for<kMaxNa>([&](auto I) {
       constexpr int na = decltype(I)::value + 1;
       if (active == na) {
-        wide_pass<DT, na, GATEUP, S, NAMAX, W8>(g, lds_ring, a_src, bptr, scale, nchunks, wave,
+        wide_pass<DT, na, GATEUP, S, NAMAX, W8>(g, lds_ring, a_src, bptr, scale, nchunks, rot, wave,
                                                 lane, lr, lh, m_start + r0, rows_pass, col0);
       }
     });
