@@ -47,6 +47,9 @@ constexpr int kBlk = 32;                 // MX block
 #ifndef MOE_MX_STAGES
 #define MOE_MX_STAGES 2
 #endif
+#ifndef MOE_MX_ROT
+#define MOE_MX_ROT 1
+#endif
 #ifndef MOE_MX_WIDE_NA
 #define MOE_MX_WIDE_NA 2
 #endif
@@ -115,7 +118,7 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 template <int NA, int NAS>
 __device__ __forceinline__ void mx_pass(const uint8_t* const* asrc, const uint8_t* const* ascale,
                                         int a_row, int a_seg, const uint8_t* const* bptr,
-                                        const uint8_t* const* bscale, int nch, int rows_pass,
+                                        const uint8_t* const* bscale, int nch, int rot, int rows_pass,
                                         int lr, int lh, uint8_t (*lds)[32 * NAS][kLdsRow],
                                         f32x16* acc) {
   constexpr int S = kStages;
@@ -124,7 +127,9 @@ __device__ __forceinline__ void mx_pass(const uint8_t* const* asrc, const uint8_
   u32x4 aring[S][2 * NA];
   MxChunk<NA> ring[S];
 
-  auto load_chunk = [&](int c, int slot) __attribute__((always_inline)) {
+  auto load_chunk = [&](int ci, int slot) __attribute__((always_inline)) {
+    int c = ci + rot;                       // chunks are walked from `rot` on
+    if (c >= nch) c -= nch;
     // Unconditional: the staging rows past the pass's rows read row 0 (in
     // bounds) and fill LDS rows whose results are never stored; a branch
     // here would split the step and let the compiler move the MFMAs.
@@ -246,6 +251,8 @@ __global__ __launch_bounds__(kThreads) void mx_grouped_kernel(MxGroupedArgs g) {
   const int a_seg = tid & 15;
   const int a_row = tid >> 4;
   const int nch = g.kd / kCK;
+  // start of the reduction walk, rotated for prefill-sized blocks only
+  const int rot = MOE_MX_ROT && NAMAX > 1 ? natural % nch : 0;
   for (int r0 = 0; r0 < rows; r0 += 32 * NAMAX) {
     if (r0 > 0) __syncthreads();
     const int rows_pass = min(32 * NAMAX, rows - r0);
@@ -268,7 +275,8 @@ __global__ __launch_bounds__(kThreads) void mx_grouped_kernel(MxGroupedArgs g) {
     f32x16 acc[2 * NAMAX];
     auto run = [&](auto NAC) __attribute__((always_inline)) {
       constexpr int na = decltype(NAC)::value;
-      mx_pass<na, NAMAX>(asrc, ascale, a_row, a_seg, bptr, bscale, nch, rows_pass, lr, lh, lds, acc);
+      mx_pass<na, NAMAX>(asrc, ascale, a_row, a_seg, bptr, bscale, nch, rot, rows_pass, lr, lh, lds,
+                         acc);
 #pragma unroll
       for (int q = 0; q < na; ++q) {
 #pragma unroll

@@ -44,6 +44,9 @@ constexpr int kLdsRow = kCK + 16;        // bytes per LDS A row (16 bytes of pad
 #ifndef MOE_W4_STAGES
 #define MOE_W4_STAGES 2
 #endif
+#ifndef MOE_W4_ROT
+#define MOE_W4_ROT 1
+#endif
 #ifndef MOE_W4_GEMM_WG
 #define MOE_W4_GEMM_WG 256
 #endif
@@ -119,7 +122,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <bool SWAP, int NA, int NAS, int S>
 __device__ __forceinline__ void w4a8_pass(const int8_t* const* asrc, int a_row, int a_seg,
                                           const uint8_t* const* bptr, int c_begin, int nch,
-                                          int rows_pass, int lr, int lh,
+                                          int rot, int rows_pass, int lr, int lh,
                                           uint8_t (*lds)[32 * NAS][kLdsRow], i32x16* acc) {
 #pragma unroll
   for (int q = 0; q < 2 * NA; ++q) acc[q] = i32x16{};
@@ -127,7 +130,9 @@ __device__ __forceinline__ void w4a8_pass(const int8_t* const* asrc, int a_row, 
   W4Chunk bring[S];
 
   auto load_chunk = [&](int i, int slot) __attribute__((always_inline)) {
-    const int64_t c = c_begin + i;
+    int ii = i + rot;                       // chunks are walked from `rot` on
+    if (ii >= nch) ii -= nch;
+    const int64_t c = c_begin + ii;
 #pragma unroll
     for (int q = 0; q < 2 * NA; ++q) {
       if (a_row + 16 * q < rows_pass) {
@@ -263,6 +268,11 @@ __global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g)
   const int a_seg = tid & 15;     // 16-byte segment of a 256-byte row chunk
   const int a_row = tid >> 4;     // 0..15 (+ 16 sb + 32 q)
   const int nch = g.kd / kCK;
+  // Start of the reduction walk: with prefill-sized blocks, workgroups
+  // streaming at one time begin at different chunks, so rows a power of two
+  // apart do not load the same columns together (measured: faster there,
+  // slower for decode-sized blocks).
+  const int rot = MOE_W4_ROT && NAMAX > 1 ? natural % nch : 0;   // prefill-sized blocks only
   for (int r0 = 0; r0 < rows; r0 += 32 * NAMAX) {
     if (r0 > 0) __syncthreads();  // every wave is done with the LDS tile
     const int rows_pass = min(32 * NAMAX, rows - r0);
@@ -277,7 +287,8 @@ __global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g)
     i32x16 acc[2 * NAMAX];
     auto epilogue = [&](auto NAC) __attribute__((always_inline)) {
       constexpr int na = decltype(NAC)::value;
-      w4a8_pass<false, na, NAMAX, kStages>(asrc, a_row, a_seg, bptr, 0, nch, rows_pass, lr, lh, lds, acc);
+      w4a8_pass<false, na, NAMAX, kStages>(asrc, a_row, a_seg, bptr, 0, nch, rot, rows_pass, lr, lh,
+                                            lds, acc);
 #pragma unroll
       for (int q = 0; q < na; ++q) {
 #pragma unroll
@@ -348,7 +359,8 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(const int8_t* __res
       asrc[sb] = A + static_cast<int64_t>(r0 + r) * K + a_seg * 16;
     }
     i32x16 acc[2];
-    w4a8_pass<true, 1, 1, kGemmStages>(asrc, a_row, a_seg, bptr, c_begin, nch, rows_pass, lr, lh, lds, acc);
+    w4a8_pass<true, 1, 1, kGemmStages>(asrc, a_row, a_seg, bptr, c_begin, nch, 0, rows_pass, lr, lh,
+                                       lds, acc);
     // lane l: activation row m = r0 + l % 32; weight rows n0 + 32 j + 8(i/4) + 4(l/32) + i%4
     const int m = r0 + lr;
     if (m < M) {
