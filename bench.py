@@ -79,7 +79,7 @@ def counter_traffic():
     return float(val.group(1))
 
 
-def workload_numbers(d, tables_sizes, weights="16bit"):
+def workload_numbers(d, tables_sizes, weights="16bit", weighted_down=False):
     """Algorithmic FLOPs and bytes of one step, per kernel (units in the
     design notes): weights of the experts that receive rows once (FP8: 1
     byte each, W4A8: half a byte, plus a 4-byte scale per row), x read once,
@@ -107,6 +107,9 @@ def workload_numbers(d, tables_sizes, weights="16bit"):
         out["gate_up_bytes"] = w_gate_up + T * H * b + n_valid * D * b
         out["down_bytes"] = w_down + n_valid * D * b + n_valid * H * b
     out["reduce_bytes"] = n_valid * H * b + T * H * b + P * 8
+    if weighted_down:   # the down GEMM reads a weight per row; the reduce reads none
+        out["down_bytes"] += n_valid * 4
+        out["reduce_bytes"] -= P * 4
     out["dispatch_bytes"] = P * 8 + n_valid * 12 + P * 8 + 12 * E
     out["flops_gate_up"] = 4 * n_valid * H * D
     out["flops_down"] = 2 * n_valid * H * D
@@ -115,12 +118,14 @@ def workload_numbers(d, tables_sizes, weights="16bit"):
     return out
 
 
-def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit"):
+def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit", weighted_down=False):
     """One workload's step timed kernel by kernel. weights "fp8" / "w4a8":
     the expert weights are quantized once (moe_quantize_fp8_rows /
     moe_quantize_int4_rows, timed on its own, not part of the step) and the
     step runs the FP8-weight GEMMs, or the W4A8 path (x and h quantised to
-    int8 inside the step, each a timed kernel of its own)."""
+    int8 inside the step, each a timed kernel of its own). weighted_down
+    (16-bit weights): the routing weight applied in the down GEMM's
+    epilogue, then an unweighted reduce."""
     import torch
 
     import mixture_experts_routed_moe_amd as mr
@@ -189,9 +194,12 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit"):
             else:
                 mr.moe_expert_gate_up(x, wg, wu, tables, h=h)
                 ev[2].record()
-                mr.moe_expert_down(h, wd, tables, expert_out=eo)
+                if weighted_down:
+                    mr.moe_expert_down_weighted(h, wd, tables, expert_out=eo)
+                else:
+                    mr.moe_expert_down(h, wd, tables, expert_out=eo)
             ev[3].record()
-        mr.moe_reduce_fused(eo, pos, wt, y=y)
+        mr.moe_reduce_fused(eo, pos, None if weighted_down else wt, y=y)
         ev[len(names)].record()
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
@@ -209,7 +217,7 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit"):
            for j, n in enumerate(names)}
     span = sum(ev[0].elapsed_time(ev[len(names)]) for ev in events) / steps
     sizes = tables.group_sizes.cpu()
-    nums = workload_numbers(d, sizes, weights)
+    nums = workload_numbers(d, sizes, weights, weighted_down)
     return dict(d=d, tables=tables, block_m=block_m, wall_ms=wall_ms, event_ms=span,
                 kernel_ms=per, nums=nums, gen_s=t_gen, quant_ms=quant_ms, weights=weights)
 
@@ -562,6 +570,18 @@ def main():
                               "activations, E8M0 scales per 32 values)")
             mx["T%d" % S.CONFIGS[ci]["T"]] = sm
         extras["mx"] = mx
+        wdn = {}
+        for ci in (2, 3):
+            rw = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev,
+                               weighted_down=True)
+            rw.pop("d")
+            rw.pop("tables")
+            torch.cuda.empty_cache()
+            sw = summarize(rw)
+            sw["workload"] = (S.CONFIGS[ci]["name"] + " with the routing weight in the down "
+                              "epilogue and an unweighted reduce")
+            wdn["T%d" % S.CONFIGS[ci]["T"]] = sw
+        extras["weighted_down"] = wdn
         extras["w4a8_gemm"] = time_w4a8_gemm(args.steps, args.warmup, dev)
         torch.cuda.empty_cache()
         print("# %s" % json.dumps(extras), file=sys.stderr, flush=True)
@@ -598,6 +618,7 @@ def main():
         "fp8_weights": extras.get("fp8_weights"),
         "w4a8": extras.get("w4a8"),
         "w4a8_gemm": extras.get("w4a8_gemm"),
+        "weighted_down": extras.get("weighted_down"),
         "mx": extras.get("mx"),
         "cpu_baseline": cpu,
     }

@@ -200,6 +200,18 @@ moe_status moe_expert_gate_up(const void* x, const void* w_gate, const void* w_u
 moe_status moe_expert_down(const void* h, const void* w_down, const moe_tables* tables, int H,
                            int D, int dtype, void* expert_out, void* stream);
 
+/* Step 2b with the routing weight in the epilogue ([B] moe_routed_kernel,
+ * second kernel: each output row is multiplied by its row weight before it
+ * is written, so the combine needs no weights):
+ *   expert_out[i, c] = R( sorted_weight[i] * (h[i] . w_down[e, c]) ),
+ * the product taken in fp32 on the accumulated dot product, then rounded
+ * once to dtype. sorted_weight comes from the tables (moe_dispatch's copy
+ * of topk_weights; all ones if it was given NULL). Feed the result to
+ * moe_reduce_fused with topk_weights = NULL.
+ * Same arguments, requirements and errors as moe_expert_down. */
+moe_status moe_expert_down_weighted(const void* h, const void* w_down, const moe_tables* tables,
+                                    int H, int D, int dtype, void* expert_out, void* stream);
+
 /* Workspace of moe_routed_forward: h [P, D] at offset 0, then expert_out
  * [P, H] at the next 256-byte boundary (both of dtype). 0 if invalid. */
 size_t moe_forward_workspace_bytes(int T, int K, int H, int D, int dtype);
@@ -215,6 +227,19 @@ moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_u
                               const void* w_down, const moe_tables* tables, int H, int D,
                               int dtype, void* workspace, size_t workspace_bytes, void* y,
                               void* stream);
+
+/* Steps 2-3 with the weighted down epilogue ([B] moe_routed_kernel):
+ *   y [T, H] dtype = moe_reduce_fused(moe_expert_down_weighted(
+ *                        moe_expert_gate_up(x)), token_topk_to_pos, NULL),
+ * i.e. y[t] = R( sum over k ascending with pos[t,k] >= 0 of
+ *                R(w[t,k] * (h . w_down)) ) in fp32. The two forms round at
+ * different points, so their results may differ in the last bits; both are
+ * deterministic. Same workspace (its expert_out then holds weighted rows),
+ * requirements and errors as moe_routed_forward. */
+moe_status moe_routed_forward_weighted(const void* x, const void* w_gate, const void* w_up,
+                                       const void* w_down, const moe_tables* tables, int H,
+                                       int D, int dtype, void* workspace,
+                                       size_t workspace_bytes, void* y, void* stream);
 
 /* Quantised expert weights (FP8 E4M3 with one fp32 scale per weight row,
  * i.e. per output channel; activations, h, expert_out and y stay in the

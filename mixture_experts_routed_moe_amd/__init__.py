@@ -24,6 +24,7 @@ __all__ = ["MoeError", "MoeTables", "FP8Weights", "default_block_m", "moe_gate",
            "quantize_fp8_rows", "moe_expert_gate_up_w8", "moe_expert_down_w8",
            "moe_routed_forward_w8", "moe_expert_gate_up",
            "moe_expert_down", "moe_routed_forward", "moe_reduce_fused", "forward_workspace",
+           "moe_expert_down_weighted", "moe_routed_forward_weighted",
            "W4Weights", "quantize_int8_rows", "quantize_int4_rows", "w4a8_gemm",
            "moe_expert_gate_up_w4a8", "moe_expert_down_w4a8", "forward_w4a8_workspace",
            "moe_routed_forward_w4a8", "MX_FP8", "MX_FP4", "MXWeights", "quantize_mx_rows",
@@ -206,17 +207,28 @@ def moe_expert_gate_up(x, w_gate, w_up, tables, h=None):
     return h
 
 
-def moe_expert_down(h, w_down, tables, expert_out=None):
-    """Step 2b: expert_out [T*K, H] = h W_down^T per sorted row (unweighted)."""
+def _down(fn, h, w_down, tables, expert_out):
     _check_tensor(h, "h", None, 2, tables.device)
     _check_tensor(w_down, "w_down", h.dtype, 3, tables.device)
     H, D = _expert_shapes(h, w_down, None, None, tables, False)
     if expert_out is None:
         expert_out = torch.empty(tables.T * tables.K, H, dtype=h.dtype, device=h.device)
     _check_tensor(expert_out, "expert_out", h.dtype, 2, tables.device)
-    check(lib().moe_expert_down(_ptr(h), _ptr(w_down), tables.ref, H, D, _DTYPE_CODE[h.dtype],
-                                _ptr(expert_out), _stream(h.device)))
+    check(fn(_ptr(h), _ptr(w_down), tables.ref, H, D, _DTYPE_CODE[h.dtype], _ptr(expert_out),
+             _stream(h.device)))
     return expert_out
+
+
+def moe_expert_down(h, w_down, tables, expert_out=None):
+    """Step 2b: expert_out [T*K, H] = h W_down^T per sorted row (unweighted)."""
+    return _down(lib().moe_expert_down, h, w_down, tables, expert_out)
+
+
+def moe_expert_down_weighted(h, w_down, tables, expert_out=None):
+    """Step 2b with the routing weight in the epilogue: expert_out row i =
+    R(sorted_weight[i] * (h[i] W_down^T)); combine with moe_reduce_fused and
+    no weights."""
+    return _down(lib().moe_expert_down_weighted, h, w_down, tables, expert_out)
 
 
 def forward_workspace(tables, H, D, dtype):
@@ -233,9 +245,12 @@ def forward_workspace(tables, H, D, dtype):
     return ws, h, eo
 
 
-def moe_routed_forward(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
+def moe_routed_forward(x, w_gate, w_up, w_down, tables, y=None, workspace=None,
+                       weighted_down=False):
     """Steps 2-3: y [T, H] of x.dtype. `workspace` from forward_workspace()
-    (allocated here when None)."""
+    (allocated here when None). weighted_down=True applies the routing
+    weights in the down GEMM's epilogue and sums the rows unweighted
+    (moe_routed_forward_weighted)."""
     _check_tensor(x, "x", None, 2, tables.device)
     for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _check_tensor(w, n, x.dtype, 3, tables.device)
@@ -247,10 +262,16 @@ def moe_routed_forward(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
         y = torch.empty(tables.T, H, dtype=x.dtype, device=x.device)
     _check_tensor(y, "y", x.dtype, 2, tables.device)
     _require(tuple(y.shape) == (tables.T, H), MOE_ERR_SHAPE, "y must be [T, H]")
-    check(lib().moe_routed_forward(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), tables.ref,
-                                   H, D, _DTYPE_CODE[x.dtype], _ptr(workspace),
-                                   workspace.numel(), _ptr(y), _stream(x.device)))
+    fn = lib().moe_routed_forward_weighted if weighted_down else lib().moe_routed_forward
+    check(fn(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), tables.ref, H, D,
+             _DTYPE_CODE[x.dtype], _ptr(workspace), workspace.numel(), _ptr(y),
+             _stream(x.device)))
     return y
+
+
+def moe_routed_forward_weighted(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
+    """Steps 2-3 with the weighted down epilogue and an unweighted combine."""
+    return moe_routed_forward(x, w_gate, w_up, w_down, tables, y, workspace, True)
 
 
 class FP8Weights:

@@ -295,6 +295,17 @@ moe_status moe_expert_down(const void* h, const void* w_down, const moe_tables* 
                     "moe_expert_down launch");
 }
 
+moe_status moe_expert_down_weighted(const void* h, const void* w_down, const moe_tables* tables,
+                                    int H, int D, int dtype, void* expert_out, void* stream) {
+  if (!h || !w_down || !expert_out) return fail(MOE_ERR_NULL, "h, w_down and expert_out must not be NULL");
+  moe_status s = check_expert_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  moe::GemmProblem p{h, w_down, nullptr, expert_out, H, D, dtype};
+  p.row_w = tables->sorted_weight;
+  return hip_status(moe::launch_down(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_down_weighted launch");
+}
+
 size_t moe_forward_workspace_expert_out_offset(int T, int K, int H, int D, int dtype) {
   if (T < 1 || K < 1 || H <= 0 || D <= 0 || !is_float(dtype)) return 0;
   return align_up(ws_h_bytes(T, K, D, dtype));
@@ -306,10 +317,12 @@ size_t moe_forward_workspace_bytes(int T, int K, int H, int D, int dtype) {
   return off + align_up(static_cast<size_t>(T) * K * H * dtype_bytes(dtype));
 }
 
-moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_up,
-                              const void* w_down, const moe_tables* tables, int H, int D,
-                              int dtype, void* workspace, size_t workspace_bytes, void* y,
-                              void* stream) {
+// The 16-bit / fp32 forward; weighted_down selects where the routing weight
+// is applied (the down epilogue, then an unweighted sum, or the reduce).
+static moe_status routed_forward(const void* x, const void* w_gate, const void* w_up,
+                                 const void* w_down, const moe_tables* tables, int H, int D,
+                                 int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                 void* stream, bool weighted_down) {
   if (!x || !w_gate || !w_up || !w_down || !workspace || !y) {
     return fail(MOE_ERR_NULL, "x, w_gate, w_up, w_down, workspace and y must not be NULL");
   }
@@ -330,12 +343,30 @@ moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_u
   hipError_t err = moe::launch_gate_up(up, *tables, st);
   if (err != hipSuccess) return hip_status(err, "moe_routed_forward gate/up launch");
   moe::GemmProblem down{hbuf, w_down, nullptr, eo, H, D, dtype};
+  if (weighted_down) down.row_w = tables->sorted_weight;
   err = moe::launch_down(down, *tables, st);
   if (err != hipSuccess) return hip_status(err, "moe_routed_forward down launch");
   const int64_t P = static_cast<int64_t>(tables->T) * tables->K;
-  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
-                           nullptr, tables->T, tables->K, H, dtype, dtype, y, st);
+  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos,
+                           weighted_down ? nullptr : tables->topk_weights, nullptr, nullptr,
+                           tables->T, tables->K, H, dtype, dtype, y, st);
   return hip_status(err, "moe_routed_forward reduce launch");
+}
+
+moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_up,
+                              const void* w_down, const moe_tables* tables, int H, int D,
+                              int dtype, void* workspace, size_t workspace_bytes, void* y,
+                              void* stream) {
+  return routed_forward(x, w_gate, w_up, w_down, tables, H, D, dtype, workspace,
+                        workspace_bytes, y, stream, false);
+}
+
+moe_status moe_routed_forward_weighted(const void* x, const void* w_gate, const void* w_up,
+                                       const void* w_down, const moe_tables* tables, int H,
+                                       int D, int dtype, void* workspace,
+                                       size_t workspace_bytes, void* y, void* stream) {
+  return routed_forward(x, w_gate, w_up, w_down, tables, H, D, dtype, workspace,
+                        workspace_bytes, y, stream, true);
 }
 
 moe_status moe_quantize_fp8_rows(const void* w, int64_t rows, int cols, int dtype, uint8_t* q,

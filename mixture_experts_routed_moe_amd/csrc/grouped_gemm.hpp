@@ -105,6 +105,7 @@ struct GemmArgs {
   const void* b1;
   const float* s0;     // W8: fp32 scale per row of b0 / b1 (one per output channel)
   const float* s1;
+  const float* row_w;  // down: routing weight per output row, or nullptr
   uint16_t* c;
   const int32_t* sorted_token;
   const int32_t* group_sizes;
@@ -244,7 +245,8 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
                                           const uint16_t* const* asrc,
                                           const uint8_t* const* bptr, const float* scale,
                                           int nchunks, int rot, int a_row, int a_seg, int lr,
-                                          int lh, int64_t out_row0, int rows_pass, int col0) {
+                                          int lh, int64_t out_row0, int rows_pass, int col0,
+                                          const float* wrow) {
   f32x16 acc[NA][2];
 #pragma unroll
   for (int q = 0; q < NA; ++q) {
@@ -328,6 +330,9 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
 
   // Epilogue. MFMA 32x32 accumulator layout: lane l holds column l % 32 and,
   // in register i, row 8*(i/4) + 4*(l/32) + i%4 of the 32x32 tile.
+  // Down with routing weights: the pass's row weights were staged in LDS
+  // (wrow) before the main loop, whose barriers made them visible.
+  const bool weighted = !GATEUP && g.row_w != nullptr;
 #pragma unroll
   for (int q = 0; q < NA; ++q) {
 #pragma unroll
@@ -343,6 +348,11 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
         if constexpr (GATEUP) {
           out[0] = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
         } else {
+          if (weighted) {   // the row's routing weight, before the rounding
+            const float w = wrow[row];
+            v0 *= w;
+            v1 *= w;
+          }
           out[0] = static_cast<uint16_t>(from_float<DT>(v0));
           out[32] = static_cast<uint16_t>(from_float<DT>(v1));
         }
@@ -385,6 +395,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   const int lr = lane & 31;
   const int lh = lane >> 5;
 
+  // Down with routing weights: the block's row weights (block_m <= 64 here),
+  // staged in LDS for the epilogue.
+  __shared__ float wrow_s[GATEUP ? 1 : 64];
+  if (!GATEUP && g.row_w != nullptr && tid < rows) wrow_s[tid] = g.row_w[m_start + tid];
+
   const int64_t kd = g.kd;
   int col0;
   const uint8_t* bptr[2];
@@ -424,10 +439,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     const int64_t out_row0 = m_start + r0;
     if (active == RG) {
       gemm_pass<DT, RG, RG, GATEUP, S, W8, CK>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
-                                           a_seg, lr, lh, out_row0, rows_pass, col0);
+                                           a_seg, lr, lh, out_row0, rows_pass, col0,
+                                           wrow_s + r0);
     } else if constexpr (RG == 2) {
       gemm_pass<DT, 1, RG, GATEUP, S, W8, CK>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
-                                          a_seg, lr, lh, out_row0, rows_pass, col0);
+                                          a_seg, lr, lh, out_row0, rows_pass, col0,
+                                          wrow_s + r0);
     }
   }
 }
@@ -492,7 +509,8 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
                                           const uint16_t* const* a_src,
                                           const uint8_t* const* bptr, const float* scale,
                                           int nchunks, int rot, int wave, int lane, int lr,
-                                          int lh, int64_t out_row0, int rows, int col0) {
+                                          int lh, int64_t out_row0, int rows, int col0,
+                                          const float* wrow) {
   constexpr int kStage = NAMAX * 4 * kAGroupElems;
   constexpr int kB = 2 * BChunk<DT, W8>::kVec;   // weight loads per chunk per wave
   constexpr int kOps = NA + kB;                   // vector memory ops per chunk per wave
@@ -598,6 +616,9 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
     }
   });
 
+  // Down with routing weights: the pass's row weights were staged in LDS
+  // (wrow) before the main loop, whose barriers made them visible.
+  const bool weighted = !GATEUP && g.row_w != nullptr;
 #pragma unroll
   for (int q = 0; q < NA; ++q) {
 #pragma unroll
@@ -613,6 +634,11 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
         if constexpr (GATEUP) {
           out[0] = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
         } else {
+          if (weighted) {   // the row's routing weight, before the rounding
+            const float w = wrow[row];
+            v0 *= w;
+            v1 *= w;
+          }
           out[0] = static_cast<uint16_t>(from_float<DT>(v0));
           out[32] = static_cast<uint16_t>(from_float<DT>(v1));
         }
@@ -644,6 +670,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
   const int wave = tid >> 6;
   const int lr = lane & 31;
   const int lh = lane >> 5;
+  // Down with routing weights: the block's row weights (<= 256 rows),
+  // staged in LDS for the epilogue.
+  __shared__ float wrow_s[GATEUP ? 1 : kThreads];
+  if (!GATEUP && g.row_w != nullptr && tid < rows) wrow_s[tid] = g.row_w[m_start + tid];
   const int64_t kd = g.kd;
   const int nchunks = g.kd / kChunkK;
   // Start of the reduction walk, as in grouped_gemm_kernel but by column
@@ -682,7 +712,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
       constexpr int na = decltype(I)::value + 1;
       if (active == na) {
         wide_pass<DT, na, GATEUP, S, NAMAX, W8>(g, lds_ring, a_src, bptr, scale, nchunks, rot, wave,
-                                                lane, lr, lh, m_start + r0, rows_pass, col0);
+                                                lane, lr, lh, m_start + r0, rows_pass, col0,
+                                                wrow_s + r0);
       }
     });
   };
@@ -733,6 +764,7 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
   g.b1 = p.b1;
   g.s0 = p.s0;
   g.s1 = p.s1;
+  g.row_w = GATEUP ? nullptr : p.row_w;
   g.c = static_cast<uint16_t*>(p.c);
   g.sorted_token = t.sorted_token;
   g.group_sizes = t.group_sizes;

@@ -4,7 +4,8 @@
 // walkthrough, sections "stage-1 gate+up" and "stage-2 down"), on fp32
 // inputs with no intermediate rounding:
 //   gate/up: h[i, j]  = SiLU(x_t . Wg[e, j]) * (x_t . Wu[e, j])
-//   down:    eo[i, c] = h[i] . Wd[e, c]
+//   down:    eo[i, c] = h[i] . Wd[e, c]   (times the row's routing weight
+//            when the weighted-epilogue form is asked for)
 // A plain vector-ALU kernel, written for checkability rather than speed:
 // every output element is one thread's fmaf chain over the reduction in
 // ascending order. A workgroup computes a 32-row x 64-column tile of one
@@ -26,6 +27,7 @@ struct F32Args {
   const float* a;
   const float* b0;
   const float* b1;
+  const float* row_w;   // down: routing weight per output row, or nullptr
   float* c;
   const int32_t* sorted_token;
   const int32_t* group_sizes;
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args g) {
         if constexpr (GATEUP) {
           out[0] = silu_f32(acc[0][i]) * acc[1][i];
         } else {
-          out[0] = acc[0][i];
+          out[0] = g.row_w ? acc[0][i] * g.row_w[m_start + r0 + r] : acc[0][i];
         }
       }
     }
@@ -133,6 +135,7 @@ hipError_t launch(const GemmProblem& p, const moe_tables& t, hipStream_t stream)
   g.a = static_cast<const float*>(p.a);
   g.b0 = static_cast<const float*>(p.b0);
   g.b1 = static_cast<const float*>(p.b1);
+  g.row_w = GATEUP ? nullptr : p.row_w;
   g.c = static_cast<float*>(p.c);
   g.sorted_token = t.sorted_token;
   g.group_sizes = t.group_sizes;

@@ -23,6 +23,10 @@ struct GemmProblem {
   int dtype;             // kF16 / kBF16 / kF32
   const float* s0 = nullptr;   // FP8 weights: fp32 scale per row of b0
   const float* s1 = nullptr;   // FP8 weights: fp32 scale per row of b1
+  // down only: fp32 routing weight per output row (the tables'
+  // sorted_weight), multiplied into each dot product before the rounding to
+  // dtype; nullptr = unweighted rows.
+  const float* row_w = nullptr;
 };
 
 hipError_t launch_gate_up(const GemmProblem& p, const moe_tables& t, hipStream_t stream);

@@ -42,6 +42,7 @@ def lib():
         L.oracle_expert_pair.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, f32p, f32p]
         L.oracle_moe_forward.argtypes = [i32, vp, vp, vp, vp, i32p, f32p, i32, i32, i32,
                                          i32, i32, i32p, i32, f32p, f32p, f32p]
+        L.oracle_moe_forward_weighted_down.argtypes = L.oracle_moe_forward.argtypes
         L.oracle_reduce.argtypes = [i32, vp, i64, i32p, f32p, i32, i32, i32, f32p]
         L.oracle_reduce_scaled.argtypes = [i32, vp, i64, i32p, f32p, f32p, f32p, i32, i32, i32,
                                            f32p]
@@ -153,11 +154,13 @@ def expert_pair(dt, x, wg, wu, wd, token, expert):
     return h, eo
 
 
-def moe_forward(dt, x, wg, wu, wd, ids, w, tokens=None, want_pairs=False):
+def moe_forward(dt, x, wg, wu, wd, ids, w, tokens=None, want_pairs=False, weighted_down=False):
     """oracle_moe_forward: y [n_tokens, H] fp32 (and per-slot h / expert_out).
 
     x [T, H]; wg, wu [E, D, H]; wd [E, H, D] (storage of dtype dt);
     ids int32 [T, K]; w fp32 [T, K]; tokens: optional token subset.
+    weighted_down: oracle_moe_forward_weighted_down (the routing weight
+    applied to the down output before its rounding, an unweighted combine).
     """
     x, wg, wu, wd = (_storage(a, dt) for a in (x, wg, wu, wd))
     ids = _c(ids, np.int32)
@@ -170,8 +173,9 @@ def moe_forward(dt, x, wg, wu, wd, ids, w, tokens=None, want_pairs=False):
     y = np.empty((n, H), np.float32)
     hp = np.empty((n * K, D), np.float32) if want_pairs else None
     ep = np.empty((n * K, H), np.float32) if want_pairs else None
-    rc = lib().oracle_moe_forward(dt, _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(ids), _ptr(w),
-                                  T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
+    fn = lib().oracle_moe_forward_weighted_down if weighted_down else lib().oracle_moe_forward
+    rc = fn(dt, _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(ids), _ptr(w), T, H, D, E, K,
+            _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
     if rc != 0:
         raise ValueError("oracle_moe_forward rejected its arguments")
     return (y, hp, ep) if want_pairs else y

@@ -184,11 +184,15 @@ struct ExpertWeights {
 //   h_j  = R(SiLU(g_j) * u_j)                    ([A] stage-1 epilogue)
 //   eo_c = R(s_d[e,c] * sum_j Wd[e,c,j] h_j)     ([A] stage-2, unweighted)
 // (the scale factors apply to FP8 weights: each dot product runs over the
-// decoded FP8 values, then is multiplied by its row's scale once). W_gate /
+// decoded FP8 values, then is multiplied by its row's scale once). With
+// row_w non-NULL the down output is weighted before its rounding,
+//   eo_c = R(w * (s_d[e,c] * sum_j Wd[e,c,j] h_j)),  w = *row_w
+// ([B] moe_routed_kernel: the down kernel multiplies each output row by the
+// row's routing weight before writing it). W_gate /
 // W_up are [E, D, H] and W_down is [E, H, D], row-major, so each dot product
 // walks a contiguous row ([A] "forward": stacked expert weights).
 void expert_pair(int dt, const float* xrow, const ExpertWeights& W, int e, int H, int D,
-                 float* hbuf, float* eo) {
+                 float* hbuf, float* eo, const float* row_w = nullptr) {
   for (int j = 0; j < D; ++j) {
     const int64_t row = (static_cast<int64_t>(e) * D + j) * H;
     float g = 0.0f, u = 0.0f;
@@ -205,14 +209,19 @@ void expert_pair(int dt, const float* xrow, const ExpertWeights& W, int e, int H
     float o = 0.0f;
     for (int j = 0; j < D; ++j) o = std::fma(load_elem(W.wdt, W.wd, row + j), hbuf[j], o);
     if (W.sd) o = o * W.sd[static_cast<int64_t>(e) * H + c];
+    if (row_w) o = o * *row_w;
     eo[c] = round_to(dt, o);
   }
 }
 
-// The full forward over a token list (see oracle_moe_forward).
+// The full forward over a token list (see oracle_moe_forward). With
+// weighted_down the routing weight is applied in the down output (above) and
+// the combine is a plain fp32 sum in k order; otherwise the combine is the
+// fma of each weight with the unweighted output, in k order.
 int moe_forward(int dt, const void* x, const ExpertWeights& W, const int32_t* ids,
                 const float* w, int T, int H, int D, int E, int K, const int32_t* tokens,
-                int n_tokens, float* y, float* h_pairs, float* eo_pairs) {
+                int n_tokens, float* y, float* h_pairs, float* eo_pairs,
+                bool weighted_down = false) {
   if (!dtype_ok(dt) || T < 0 || H <= 0 || D <= 0 || E <= 0 || K <= 0) return -1;
   if (!tokens && n_tokens != T) return -1;
   for (int i = 0; i < n_tokens; ++i) {
@@ -239,9 +248,14 @@ int moe_forward(int dt, const void* x, const ExpertWeights& W, const int32_t* id
           if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = 0.0f;
           continue;
         }
-        expert_pair(dt, xrow.data(), W, e, H, D, hbuf.data(), eo.data());
         const float wk = w[slot];
-        for (int c = 0; c < H; ++c) acc[c] = std::fma(wk, eo[c], acc[c]);
+        expert_pair(dt, xrow.data(), W, e, H, D, hbuf.data(), eo.data(),
+                    weighted_down ? &wk : nullptr);
+        if (weighted_down) {
+          for (int c = 0; c < H; ++c) acc[c] = acc[c] + eo[c];
+        } else {
+          for (int c = 0; c < H; ++c) acc[c] = std::fma(wk, eo[c], acc[c]);
+        }
         if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = hbuf[j];
         if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = eo[c];
       }
@@ -397,6 +411,20 @@ int oracle_moe_forward(int dt, const void* x, const void* wg, const void* wu,
                        int n_tokens, float* y, float* h_pairs, float* eo_pairs) {
   const ExpertWeights W{dt, wg, wu, wd, nullptr, nullptr, nullptr};
   return moe_forward(dt, x, W, ids, w, T, H, D, E, K, tokens, n_tokens, y, h_pairs, eo_pairs);
+}
+
+// The forward with the routing weight applied in the down output and an
+// unweighted combine ([B] moe_routed_kernel's down epilogue):
+//   eo_p = R(w_p * (h_p . Wd[e]))   y[t] = sum over unmasked k ascending of eo_(t,k)
+// (fp32 adds in k order). Same arguments and outputs as oracle_moe_forward;
+// eo_pairs holds the weighted rows.
+int oracle_moe_forward_weighted_down(int dt, const void* x, const void* wg, const void* wu,
+                                     const void* wd, const int32_t* ids, const float* w, int T,
+                                     int H, int D, int E, int K, const int32_t* tokens,
+                                     int n_tokens, float* y, float* h_pairs, float* eo_pairs) {
+  const ExpertWeights W{dt, wg, wu, wd, nullptr, nullptr, nullptr};
+  return moe_forward(dt, x, W, ids, w, T, H, D, E, K, tokens, n_tokens, y, h_pairs, eo_pairs,
+                     true);
 }
 
 // ------------------------------------------------ FP8 expert weights ------

@@ -104,6 +104,12 @@ def test_calls_reject_bad_arguments_before_launching():
                                 need - 1, fake, None) == 5
     assert L.moe_expert_gate_up(fake, fake, None, ctypes.byref(s), 256, 128, 1, fake, None) == 1
     assert L.moe_expert_down(fake, fake, ctypes.byref(s), 256, 128, 0, None, None) == 1
+    assert L.moe_expert_down_weighted(fake, fake, ctypes.byref(s), 256, 128, 0, None, None) == 1
+    assert L.moe_expert_down_weighted(fake, fake, ctypes.byref(s), 256, 100, 0, fake, None) == 2
+    assert L.moe_routed_forward_weighted(fake, fake, fake, fake, ctypes.byref(s), 256, 128, 1,
+                                         fake, need - 1, fake, None) == 5
+    assert L.moe_routed_forward_weighted(fake, fake, fake, fake, ctypes.byref(s), 256, 128, 7,
+                                         fake, 1 << 30, fake, None) == 3
 
 
 def test_gate_rejects_bad_arguments_before_launching():
