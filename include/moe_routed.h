@@ -15,7 +15,9 @@
  *                              with SiLU(gate)*up fused in the epilogue,
  *      moe_expert_down      -- grouped GEMM over the stacked down weights;
  *   3. moe_reduce_fused     -- top-k weighted fp32 reduce back to token order.
- * moe_routed_forward runs step 2 and step 3 back to back.
+ * moe_routed_forward runs step 2 and step 3 back to back. The _weighted
+ * variants of the down GEMM and of the forward apply the routing weight in
+ * the down GEMM's epilogue instead, and combine with an unweighted reduce.
  *
  * Sources (page title, section):
  *   [A] "tilelang baseline" MoE walkthrough (devpress.csdn.net, tilelang-metax
