@@ -86,9 +86,12 @@ constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
 #define MOE_W8_WIDE_STAGES 4
 #endif
 #ifndef MOE_RG1_DOWN_STAGES
-#define MOE_RG1_DOWN_STAGES 2
+#define MOE_RG1_DOWN_STAGES 8
 #endif
-constexpr int kStagesRG1 = 4;
+#ifndef MOE_RG1_STAGES
+#define MOE_RG1_STAGES 6
+#endif
+constexpr int kStagesRG1 = MOE_RG1_STAGES;
 constexpr int kStagesRG1Down = MOE_RG1_DOWN_STAGES;
 constexpr int kStagesRG2 = 4;
 #ifndef MOE_WIDE_STAGES

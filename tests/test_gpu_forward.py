@@ -132,6 +132,18 @@ def test_forward_wide_blocks(block_m):
     _check_pairs(tables, h, eo, hp, ep, 2)
 
 
+@pytest.mark.parametrize("block_m", [16, 32])
+def test_forward_deep_pipeline_tails(block_m):
+    """Decode-sized blocks with reductions long enough for the deepest
+    pipelines (gate/up: 24 chunks of 64, full groups of steps and a tail;
+    down: 20 chunks) and ragged rows."""
+    d = _custom(T=70, H=1536, D=1280, E=5, K=3, dtype="bf16", seed=16, mask=0.1, hot=1)
+    tables, h, eo, y = _run(d, block_m=block_m)
+    y_ref, hp, ep = _oracle(d)
+    assert_close_16(y.float().cpu().numpy(), y_ref, "deep pipeline")
+    _check_pairs(tables, h, eo, hp, ep, 3)
+
+
 def test_forward_empty_experts_and_all_masked_tokens():
     d = _custom(T=40, H=256, D=128, E=16, K=2, dtype="bf16", seed=12)
     ids = d["topk_ids"]
