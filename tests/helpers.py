@@ -53,3 +53,43 @@ def round_like(x_f32, dtype):
 
 def gpu_available():
     return torch.cuda.is_available()
+
+
+def cover_tokens(ids, E, block_m, full_upto=512, group_rows=32, seed=0):
+    """Tokens whose rows touch every (expert, row block, 32-row group) cell of
+    the dispatch at `block_m` -- every active expert, every scheduled row
+    block, every row group of a block (so both passes of a block that takes
+    two) -- plus the first and last token. All tokens when T <= full_upto.
+
+    ids: int32 [T, K] (negative = masked). Greedy set cover over the cells
+    (ties broken by a seeded shuffle of the tokens); the rows come from the
+    oracle's dispatch, so the choice does not depend on the GPU tables."""
+    ids = np.asarray(ids, np.int32)
+    T, K = ids.shape
+    if T <= full_upto:
+        return np.arange(T, dtype=np.int32)
+    tab = oracle.dispatch(ids, None, E, block_m)
+    sizes, offs = tab["group_sizes"], tab["group_offsets"]
+    n = tab["n_valid"]
+    expert_of_row = np.repeat(np.arange(E), sizes)
+    local = np.arange(n) - offs[expert_of_row]
+    groups_per_block = (block_m + group_rows - 1) // group_rows
+    cell_of_row = (expert_of_row.astype(np.int64) * (T * K // block_m + 2) + local // block_m) \
+        * groups_per_block + (local % block_m) // group_rows
+    _, cell_of_row = np.unique(cell_of_row, return_inverse=True)
+    n_cells = int(cell_of_row.max()) + 1 if n else 0
+    pos = tab["token_topk_to_pos"]                         # [T, K]
+    tok_cells = np.where(pos >= 0, cell_of_row[np.maximum(pos, 0)], n_cells)
+    covered = np.zeros(n_cells + 1, bool)
+    covered[n_cells] = True                                # the masked-slot sentinel
+    chosen = [0, T - 1]
+    for t in chosen:
+        covered[tok_cells[t]] = True
+    order = np.random.default_rng(seed).permutation(T)
+    cand = tok_cells[order]
+    while not covered.all():
+        gain = (~covered[cand]).sum(axis=1)
+        j = int(np.argmax(gain))
+        chosen.append(int(order[j]))
+        covered[cand[j]] = True
+    return np.array(sorted(set(chosen)), np.int32)

@@ -6,8 +6,10 @@
     masked slots, empty experts and experts that overflow one row block, at
     every supported block_m;
   * the DeepSeek-shaped decode / prefill / skewed workloads at full size, in
-    the launch configuration the benchmark times, on sampled tokens the
-    oracle computes one by one.
+    the launch configuration the benchmark times: the decode workload on all
+    512 tokens, the T = 4096 workloads on a token set that puts a checked row
+    in every 32-row group of every scheduled row block of every active
+    expert (both passes of the skewed workload's 256-row blocks included).
 Outputs are pre-filled with NaN so an unwritten element fails the test.
 """
 import numpy as np
@@ -16,7 +18,8 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import ORACLE_DT, REL_L2_32, assert_close_16, gpu_available, metrics, storage
+from helpers import (ORACLE_DT, REL_L2_32, assert_close_16, cover_tokens, gpu_available,
+                     metrics, storage)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -224,17 +227,6 @@ def test_forward_fp32_ragged(block_m):
 
 # ------------------------------------------------------------ full sizes ---
 
-def _sample_tokens(d, n, seed):
-    T = d["T"]
-    ids = d["topk_ids"].cpu()
-    cnt = torch.bincount(ids.view(-1).clamp(min=0).long(), minlength=d["E"])
-    hot = int(cnt.argmax())
-    hot_tok = int((ids == hot).any(dim=1).nonzero()[0])   # a token routed to the hottest expert
-    g = torch.Generator().manual_seed(seed)
-    rand = torch.randperm(T, generator=g)[:n - 3].tolist()
-    return np.array(sorted(set([0, T - 1, hot_tok] + rand)), np.int32)
-
-
 def _sampled_oracle(d, tokens):
     """The oracle on `tokens`, given only the experts those tokens use."""
     ids = d["topk_ids"].cpu().numpy()[tokens]
@@ -258,7 +250,7 @@ def test_forward_full_size_sampled(ci):
     block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"])
     tables, h, eo, y = _run(d, block_m=block_m)
     assert not torch.isnan(y).any()
-    tokens = _sample_tokens(d, 8, seed=ci)
+    tokens = cover_tokens(d["topk_ids"].cpu().numpy(), cfg["E"], block_m)
     y_ref, hp, ep = _sampled_oracle(d, tokens)
     assert_close_16(y.float().cpu().numpy()[tokens], y_ref, cfg["name"])
     _check_pairs(tables, h, eo, hp, ep, cfg["K"], token_index=list(tokens))

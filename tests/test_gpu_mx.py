@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import ORACLE_DT, assert_close_16, gpu_available, metrics, storage
+from helpers import ORACLE_DT, assert_close_16, cover_tokens, gpu_available, metrics, storage
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -220,8 +220,7 @@ def test_forward_mx_full_size_sampled(ci):
     block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"])
     tables, h, eo, xq, xs, y = _run_mx(d, gpu, block_m=block_m)
     _check_x_quant(d, xq, xs)
-    rng = np.random.default_rng(ci)
-    tokens = np.sort(rng.choice(cfg["T"], size=12, replace=False)).astype(np.int32)
+    tokens = cover_tokens(d["topk_ids"].cpu().numpy(), cfg["E"], block_m)
     y_ref = _oracle_mx(d, ref, tokens=tokens)
     got = y.float().cpu().numpy()
     assert not np.isnan(got).any()

@@ -24,7 +24,7 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import ORACLE_DT, assert_close_16, gpu_available, metrics, storage
+from helpers import ORACLE_DT, assert_close_16, cover_tokens, gpu_available, metrics, storage
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -252,8 +252,7 @@ def test_forward_w4a8_full_size_sampled(ci):
     block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"])
     tables, h, eo, xq, sx, y = _run_w4(d, gpu, block_m=block_m)
     _check_x_quant(d, xq, sx)
-    rng = np.random.default_rng(ci)
-    tokens = np.sort(rng.choice(cfg["T"], size=16, replace=False)).astype(np.int32)
+    tokens = cover_tokens(d["topk_ids"].cpu().numpy(), cfg["E"], block_m)
     y_ref = _oracle_w4(d, ref, tokens=tokens)
     got = y.float().cpu().numpy()
     assert not np.isnan(got).any()

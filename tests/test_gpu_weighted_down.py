@@ -20,8 +20,9 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import ORACLE_DT, REL_L2_32, assert_close_16, gpu_available, metrics, storage
-from test_gpu_forward import _custom, _sample_tokens
+from helpers import (ORACLE_DT, REL_L2_32, assert_close_16, cover_tokens, gpu_available,
+                     metrics, storage)
+from test_gpu_forward import _custom
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -149,7 +150,7 @@ def test_weighted_stages_match_forward():
     assert torch.equal(eo2[:n], eo[:n]) and torch.equal(y2, y)
 
 
-@pytest.mark.parametrize("ci", [2, 3])
+@pytest.mark.parametrize("ci", [2, 3, 4])
 def test_weighted_forward_full_size_sampled(ci):
     mr = _mr()
     cfg = S.CONFIGS[ci]
@@ -157,7 +158,7 @@ def test_weighted_forward_full_size_sampled(ci):
     block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"])
     tables, h, eo, y = _run(d, block_m=block_m)
     assert not torch.isnan(y).any()
-    tokens = _sample_tokens(d, 8, seed=ci)
+    tokens = cover_tokens(d["topk_ids"].cpu().numpy(), cfg["E"], block_m)
     ids = d["topk_ids"].cpu().numpy()[tokens]
     used = np.unique(ids[ids >= 0])
     remap = np.full(d["E"], -1, np.int32)
