@@ -3,11 +3,13 @@
 Against:
   * the worked examples printed on the tilelang-baseline MoE walkthrough,
     section 'forward' (tests/golden/dispatch_toy.json);
-  * an independent brute force: numpy's stable argsort for the permutation,
-    and the walkthrough's own loops for the padded offsets (a ceil over
-    count + 1) and for the block -> expert table (a double loop over blocks
-    and experts keeping the last expert whose padded start is <= the block
-    start);
+  * an independent brute force written from the definitions of the
+    walkthrough's 'forward' section: numpy's stable argsort for the
+    permutation, the padded offsets as an exclusive prefix sum of each
+    group's span (its count plus one, rounded up to a whole number of
+    blocks), and the block -> expert table as a sorted search of each block's
+    first row among the padded starts (the last expert starting at or before
+    it);
   * invariants that hold at any size.
 """
 import json
@@ -33,20 +35,14 @@ def brute_force_tables(ids, w, E, BM):
     counts = np.bincount(flat[valid], minlength=E)[:E]
     cum = np.cumsum(counts)
     offsets = cum - counts
-    padded = [0 for _ in range(E)]
-    for i in range(1, E):
-        padded[i] = padded[i - 1] + math.ceil((counts[i - 1] + 1) / BM) * BM
-    M = math.ceil(P / BM) + E
-    blk = [0 for _ in range(M)]
-    for bx in range(M):
-        start = bx * BM
-        for i in range(E):
-            if start >= padded[i]:
-                blk[bx] = i
+    span = -(-(counts.astype(np.int64) + 1) // BM) * BM      # whole blocks, >= 1 per expert
+    padded = np.concatenate([[0], np.cumsum(span)[:-1]])
+    n_blocks = -(-P // BM) + E
+    blk = np.searchsorted(padded, np.arange(n_blocks) * BM, side="right") - 1
     pos = np.full(P, -1, np.int64)
     pos[order] = np.arange(order.size)
-    return dict(group_sizes=counts, group_offsets=offsets, group_padded_offsets=np.array(padded),
-                block_expert=np.array(blk), sorted_pair=order, sorted_token=order // K,
+    return dict(group_sizes=counts, group_offsets=offsets, group_padded_offsets=padded,
+                block_expert=blk, sorted_pair=order, sorted_token=order // K,
                 sorted_weight=w.reshape(-1)[order], token_topk_to_pos=pos.reshape(T, K),
                 n_valid=order.size)
 
