@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace moe {
 
 constexpr int kF16 = 0;
@@ -73,5 +76,27 @@ __device__ __forceinline__ uint32_t from_float(float v) {
   if constexpr (DT == kBF16) return float_to_bf16(v);
   else return float_to_f16(v);
 }
+
+template <int N>
+using int_c = std::integral_constant<int, N>;
+
+// Calls f(int_c<0>{}), ..., f(int_c<N-1>{}): a loop whose index is a
+// compile-time constant in every iteration (register-ring slots stay static).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(int_c<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// SiLU(g) = g / (1 + e^-g), in fp32.
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// A workgroup barrier that waits for no memory counter (the caller issues
+// the s_waitcnt it needs first) but is a compiler-level memory fence: no LDS
+// or global access is moved across it.
+__device__ __forceinline__ void barrier_no_wait() { asm volatile("s_barrier" ::: "memory"); }
 
 }  // namespace moe

@@ -53,9 +53,6 @@
 
 #pragma once
 
-#include <type_traits>
-#include <utility>
-
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -65,42 +62,23 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunkK = 64;
 constexpr int kLdsRow = kChunkK + 8;   // elements per LDS row (144 bytes)
-// Pipeline depths (chunks in flight), measured on MI355X: blocks of <= 32
-// rows stream gate/up best at depth 4 and down (half the bytes per column
-// tile, more workgroups) at depth 2; 64-row blocks at depth 4. The wide
-// kernel runs at depth 4 (registers: 6 row groups of accumulators, the
-// weight ring and the A ring fill the 512 registers of one wave per SIMD).
-#ifndef MOE_W8_RG1_STAGES
-#define MOE_W8_RG1_STAGES 4
-#endif
-#ifndef MOE_WIDE_ROT
-#define MOE_WIDE_ROT 1
-#endif
-#ifndef MOE_RG_ROT
-#define MOE_RG_ROT 1
-#endif
-#ifndef MOE_RG_EARLY_PREFETCH
-#define MOE_RG_EARLY_PREFETCH 0
-#endif
-#ifndef MOE_W8_WIDE_STAGES
-#define MOE_W8_WIDE_STAGES 4
-#endif
-#ifndef MOE_RG1_DOWN_STAGES
-#define MOE_RG1_DOWN_STAGES 8
-#endif
-#ifndef MOE_RG1_STAGES
-#define MOE_RG1_STAGES 6
-#endif
-constexpr int kStagesRG1 = MOE_RG1_STAGES;
-constexpr int kStagesRG1Down = MOE_RG1_DOWN_STAGES;
+// Pipeline depths (chunks in flight), measured on MI355X at the DeepSeek
+// decode shapes: blocks of <= 32 rows stream gate/up best at depth 6 (2.455
+// -> 2.443 ms from depth 4) and down at depth 8 (1.309 -> 1.271 ms from
+// depth 2; one workgroup per CU, more weight bytes in flight per wave); FP8
+// weights keep depth 4 (the FP8 down measured 0.70 -> 0.74 ms at depth 8).
+// 64-row blocks run at depth 4. The wide kernel runs at depth 4 (6 row
+// groups of accumulators, the weight ring and the A ring fill the 512
+// registers of one wave per SIMD), with FP8 weights too.
+constexpr int kStagesRG1 = 6;
+constexpr int kStagesRG1Down = 8;
+constexpr int kStagesRG1W8 = 4;
 constexpr int kStagesRG2 = 4;
-#ifndef MOE_WIDE_STAGES
-#define MOE_WIDE_STAGES 4
-#endif
-#ifndef MOE_WIDE_NAMAX
-#define MOE_WIDE_NAMAX 6
-#endif
-constexpr int kStagesWide = MOE_WIDE_STAGES;
+constexpr int kStagesWide = 4;
+constexpr int kStagesWideW8 = 4;
+// Row groups of 32 rows the wide kernel keeps in one pass over the weights
+// for 256-row blocks (5 at depth 5 measured 3.58 ms, 6 at depth 4 3.44 ms).
+constexpr int kWideNaMax = 6;
 
 struct GemmArgs {
   const uint16_t* a;
@@ -136,7 +114,6 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
 }
 
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // One chunk of a wave's weights: for each of its two weight rows, the lane's
 // CK/2 reduction elements as loaded -- 16-bit values (CK = 64: 4 x 16 bytes)
@@ -186,19 +163,7 @@ struct BChunk {
   }
 };
 
-template <int N>
-using int_c = std::integral_constant<int, N>;
 
-// Calls f(int_c<0>{}), ..., f(int_c<N-1>{}): a loop whose index is a
-// compile-time constant in every iteration (register-ring slots stay static).
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(int_c<I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // The two weight rows a lane streams and their scales: gate/up -- row col0
 // + lane%32 of W_gate and of W_up (col0 = 128*nt + 32*wave); down -- rows
@@ -302,9 +267,6 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
   auto step = [&](int c, auto U, bool prefetch, bool stage) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
     if (prefetch) load_chunk(c + S - 1, (u + S - 1) % S);
-#if MOE_RG_EARLY_PREFETCH
-    __builtin_amdgcn_sched_barrier(0);   // issue the prefetch before the MFMAs
-#endif
     constexpr int buf = u & 1;   // S is even, so c & 1 == u & 1
 #pragma unroll
     for (int t = 0; t < CK / 16; ++t) {
@@ -411,11 +373,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
 
   const int nchunks = g.kd / CK;
   // Start of the reduction walk (a rotation of the chunk order): 16-bit
-  // weights start each workgroup at chunk (MOE_RG_ROT * tile) mod nchunks,
+  // weights start each workgroup at chunk (its tile index) mod nchunks,
   // so the workgroups streaming at one time touch different columns of
   // their weight rows (rows 4 KB apart otherwise load the same columns
   // together); FP8 weights walk from chunk 0.
-  const int rot = W8 ? 0 : static_cast<int>((static_cast<int64_t>(natural) * MOE_RG_ROT) % nchunks);
+  const int rot = W8 ? 0 : static_cast<int>(static_cast<int64_t>(natural) % nchunks);
   constexpr int kASeg = CK / 8;             // 16-byte segments of an A row chunk
   constexpr int kARows = 256 / kASeg;       // A rows per pass of the threads
   constexpr int kSub = 32 / kARows;
@@ -591,7 +553,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
     static_for<S>([&](auto U) {
       constexpr int u = decltype(U)::value;
       wait_vmcnt<(S - 2) * kOps>();
-      __builtin_amdgcn_s_barrier();
+      barrier_no_wait();
       load_chunk(c0 + u + S - 1, (u + S - 1) % S);
       multiply(c0 + u, U);
       wait_vmcnt<(kB + (S - 2) * kOps < 63 ? kB + (S - 2) * kOps : 63)>();
@@ -604,7 +566,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
     constexpr int u = decltype(U)::value;
     if (u < rem) {
       wait_chunks_after<kOps, S - 2>(min(S - 2, rem - 1 - u));
-      __builtin_amdgcn_s_barrier();
+      barrier_no_wait();
       if (u + S - 1 < rem) load_chunk(c0 + u + S - 1, (u + S - 1) % S);
       multiply(c0 + u, U);
       if (u + 1 < rem) {
@@ -682,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
   // Start of the reduction walk, as in grouped_gemm_kernel but by column
   // tile: the row blocks of one expert that share a weight tile still walk
   // it together (and share it in L2), different tiles start apart.
-  const int rot = MOE_WIDE_ROT && !W8 ? nt % nchunks : 0;
+  const int rot = W8 ? 0 : nt % nchunks;
 
   int col0;
   const uint8_t* bptr[2];
@@ -724,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
     run_pass(0, int_c<NAMAX>{});
   } else {
     run_pass(0, int_c<4>{});
-    __builtin_amdgcn_s_barrier();   // every wave is done with the LDS tile
+    barrier_no_wait();   // every wave is done with the LDS tile
     run_pass(128, int_c<4>{});
   }
 }
@@ -733,7 +695,7 @@ template <int DT, bool GATEUP, int NAMAX, bool W8>
 void launch_wide(unsigned grid, const GemmArgs& g, hipStream_t stream) {
   // Depth S needs at least S chunks; a 128-long reduction (the shortest the
   // shape rules allow: 2 chunks) runs at depth 2.
-  constexpr int S = W8 ? MOE_W8_WIDE_STAGES : kStagesWide;
+  constexpr int S = W8 ? kStagesWideW8 : kStagesWide;
   if (g.kd / kChunkK >= S) {
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<DT, GATEUP, S, NAMAX, W8>), dim3(grid),
                        dim3(kThreads), 0, stream, g);
@@ -788,14 +750,14 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
   if (t.block_m <= 32) {
     // FP8 weights: 128-element chunks of the same bytes per row as the
     // 16-bit chunks, depth 4 for both GEMMs.
-    constexpr int S = W8 ? MOE_W8_RG1_STAGES : (GATEUP ? kStagesRG1 : kStagesRG1Down);
+    constexpr int S = W8 ? kStagesRG1W8 : (GATEUP ? kStagesRG1 : kStagesRG1Down);
     launch_rg<DT, 1, GATEUP, S, W8>(grid, g, stream);
   } else if (t.block_m == 64) {
     launch_rg<DT, 2, GATEUP, kStagesRG2, W8>(grid, g, stream);
   } else if (t.block_m == 128) {
     launch_wide<DT, GATEUP, 4, W8>(grid, g, stream);
   } else {
-    launch_wide<DT, GATEUP, MOE_WIDE_NAMAX, W8>(grid, g, stream);
+    launch_wide<DT, GATEUP, kWideNaMax, W8>(grid, g, stream);
   }
   return hipGetLastError();
 }

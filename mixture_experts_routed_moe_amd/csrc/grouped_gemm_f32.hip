@@ -39,7 +39,6 @@ struct F32Args {
   int n, kd, block_m, n_tiles;
 };
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args g) {
@@ -120,7 +119,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args g) {
       if (r < rows_pass) {
         float* out = g.c + static_cast<int64_t>(m_start + r0 + r) * g.n + col0 + col;
         if constexpr (GATEUP) {
-          out[0] = silu_f32(acc[0][i]) * acc[1][i];
+          out[0] = silu(acc[0][i]) * acc[1][i];
         } else {
           out[0] = g.row_w ? acc[0][i] * g.row_w[m_start + r0 + r] : acc[0][i];
         }

@@ -29,9 +29,6 @@
 // double-buffered LDS tile; their scales and the weights come straight from
 // memory into a register ring.
 
-#include <type_traits>
-#include <utility>
-
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -44,16 +41,10 @@ constexpr int kThreads = 256;
 constexpr int kCK = 256;                 // reduction elements per chunk
 constexpr int kLdsRow = kCK + 16;        // bytes per LDS row of FP8 activations
 constexpr int kBlk = 32;                 // MX block
-#ifndef MOE_MX_STAGES
-#define MOE_MX_STAGES 2
-#endif
-#ifndef MOE_MX_ROT
-#define MOE_MX_ROT 1
-#endif
-#ifndef MOE_MX_WIDE_NA
-#define MOE_MX_WIDE_NA 2
-#endif
-constexpr int kStages = MOE_MX_STAGES;
+// Weight chunks in the register ring (depth 4 measured slower at decode,
+// two workgroups per CU) and row groups per pass for 128/256-row blocks.
+constexpr int kStages = 2;
+constexpr int kWideNa = 2;
 
 // A = FP8 E4M3 (format code 0), B = FP4 E2M1 (format code 4); byte T of each
 // scale word is the E8M0 scale of the lane half's reduction block. The FP4
@@ -69,17 +60,7 @@ __device__ __forceinline__ f32x16 mfma_mx(const u32x4& a_lo, const u32x4& a_hi, 
                                                           static_cast<int>(sb));
 }
 
-template <int N>
-using int_c = std::integral_constant<int, N>;
 
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(int_c<I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // A lane's share of one chunk: its two weight rows (64 bytes of FP4 each)
 // with their 4-byte scale words, and for each of its NA activation rows the
@@ -109,7 +90,6 @@ struct MxGroupedArgs {
   int n, kd, block_m, n_tiles;
 };
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // One pass over the reduction for NA groups of 32 activation rows (LDS tile
 // of 32 * NAS rows). asrc[2q + sb]: this thread's staging row of group q
@@ -252,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void mx_grouped_kernel(MxGroupedArgs g) {
   const int a_row = tid >> 4;
   const int nch = g.kd / kCK;
   // start of the reduction walk, rotated for prefill-sized blocks only
-  const int rot = MOE_MX_ROT && NAMAX > 1 ? natural % nch : 0;
+  const int rot = NAMAX > 1 ? natural % nch : 0;
   for (int r0 = 0; r0 < rows; r0 += 32 * NAMAX) {
     if (r0 > 0) __syncthreads();
     const int rows_pass = min(32 * NAMAX, rows - r0);
@@ -421,7 +401,7 @@ hipError_t launch_grouped(const MxGemmProblem& p, const moe_tables& t, hipStream
   } else if (t.block_m == 64) {
     hipLaunchKernelGGL((mx_grouped_kernel<DT, GATEUP, 2>), dim3(grid), dim3(kThreads), 0, stream, g);
   } else {
-    hipLaunchKernelGGL((mx_grouped_kernel<DT, GATEUP, MOE_MX_WIDE_NA>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((mx_grouped_kernel<DT, GATEUP, kWideNa>), dim3(grid), dim3(kThreads),
                        0, stream, g);
   }
   return hipGetLastError();

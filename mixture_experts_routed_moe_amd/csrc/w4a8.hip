@@ -26,9 +26,6 @@
 // LDS tile; the weights stream straight from HBM into registers with a
 // 4-deep ring, as in the 16-bit grouped GEMM.
 
-#include <type_traits>
-#include <utility>
-
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -41,23 +38,14 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;
 constexpr int kCK = 256;                 // reduction elements per chunk
 constexpr int kLdsRow = kCK + 16;        // bytes per LDS A row (16 bytes of padding)
-#ifndef MOE_W4_STAGES
-#define MOE_W4_STAGES 2
-#endif
-#ifndef MOE_W4_ROT
-#define MOE_W4_ROT 1
-#endif
-#ifndef MOE_W4_GEMM_WG
-#define MOE_W4_GEMM_WG 256
-#endif
-#ifndef MOE_W4_GEMM_STAGES
-#define MOE_W4_GEMM_STAGES 4
-#endif
-#ifndef MOE_W4_WIDE_NA
-#define MOE_W4_WIDE_NA 4
-#endif
-constexpr int kStages = MOE_W4_STAGES;   // weight chunks in the register ring
-constexpr int kGemmStages = MOE_W4_GEMM_STAGES;   // the same for the plain GEMM
+// Weight chunks in the register ring of the grouped kernels (depth 4
+// measured slower at decode, two workgroups per CU) and of the plain GEMM;
+// workgroups the plain GEMM aims for (split-K); row groups per pass for
+// 128/256-row blocks.
+constexpr int kStages = 2;
+constexpr int kGemmStages = 4;
+constexpr int kGemmWorkgroups = 256;
+constexpr int kWideNa = 4;
 
 __device__ __forceinline__ i32x16 mfma_i8(u32x4 a, u32x4 b, i32x16 c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
@@ -95,17 +83,7 @@ struct W4Chunk {
   }
 };
 
-template <int N>
-using int_c = std::integral_constant<int, N>;
 
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(int_c<I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // One pass over chunks [c_begin, c_begin + nch) for NA groups of 32
 // activation rows (the LDS tile holds 32 * NAS rows, NAS >= NA).
@@ -194,7 +172,6 @@ __device__ __forceinline__ void w4a8_pass(const int8_t* const* asrc, int a_row, 
   });
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // (float) acc * s_a * s_w, left to right in fp32 (acc: the exact int32 sum).
 __device__ __forceinline__ float dequant(int acc, float sa, float sw) {
@@ -272,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g)
   // streaming at one time begin at different chunks, so rows a power of two
   // apart do not load the same columns together (measured: faster there,
   // slower for decode-sized blocks).
-  const int rot = MOE_W4_ROT && NAMAX > 1 ? natural % nch : 0;   // prefill-sized blocks only
+  const int rot = NAMAX > 1 ? natural % nch : 0;   // prefill-sized blocks only
   for (int r0 = 0; r0 < rows; r0 += 32 * NAMAX) {
     if (r0 > 0) __syncthreads();  // every wave is done with the LDS tile
     const int rows_pass = min(32 * NAMAX, rows - r0);
@@ -538,11 +515,11 @@ hipError_t launch_quantize_int4_rows(const void* w, int64_t rows, int cols, int 
 hipError_t launch_w4a8_gemm(const int8_t* A, const uint8_t* B, int M, int N, int K, int32_t* Ct,
                             hipStream_t stream) {
   // Split the reduction while the column tiles give fewer than
-  // MOE_W4_GEMM_WG workgroups, keeping at least 2 chunks per split.
+  // kGemmWorkgroups workgroups, keeping at least 2 chunks per split.
   const int col_tiles = N / 256;
   const int nch = K / kCK;
-  int per = static_cast<int>((static_cast<int64_t>(col_tiles) * nch + MOE_W4_GEMM_WG - 1) /
-                             MOE_W4_GEMM_WG);
+  int per = static_cast<int>((static_cast<int64_t>(col_tiles) * nch + kGemmWorkgroups - 1) /
+                             kGemmWorkgroups);
   per = max(2, per);
   if (per > nch) per = nch;
   const int splits = (nch + per - 1) / per;
@@ -588,7 +565,7 @@ static hipError_t launch_grouped(const W4GemmProblem& p, const moe_tables& t, hi
   } else if (t.block_m == 64) {
     hipLaunchKernelGGL((w4a8_grouped_kernel<DT, GATEUP, 2>), dim3(grid), dim3(kThreads), 0, stream, g);
   } else {
-    hipLaunchKernelGGL((w4a8_grouped_kernel<DT, GATEUP, MOE_W4_WIDE_NA>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((w4a8_grouped_kernel<DT, GATEUP, kWideNa>), dim3(grid), dim3(kThreads),
                        0, stream, g);
   }
   return hipGetLastError();
