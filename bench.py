@@ -8,12 +8,22 @@ exactly the kernels moe_routed_forward launches after the dispatch, called
 stage by stage so that HIP events (recorded on the stream the kernels run
 on) time every kernel inside the timed region.
 
-Workload (the metric's T = 512 case): the DeepSeek-shaped decode layer,
-T=512, d_hidden=7168, d_expert=2048, E=256 routed experts, top-8, bf16,
-seeded synthetic x / weights / router (no dataset, random-init weights).
-The same line also carries the metric's T = 4096 case (the prefill layer
-of the same shapes) under "t4096", and the CPU oracle timed on a bounded
-sample of the decode workload under "cpu_baseline".
+Workload of the headline value (the metric's T = 512 case): the
+DeepSeek-shaped decode layer, T=512, d_hidden=7168, d_expert=2048, E=256
+routed experts, top-8, bf16, seeded synthetic x / weights / router (no
+dataset, random-init weights). The same JSON line carries, at its end, the
+metric's T = 4096 case (the prefill layer of the same shapes, "t4096"), the
+Zipf-skewed T = 4096 routed forward ("skewed"), its standalone reduce
+("reduce_skewed"), the two small workloads and the quantised / weighted
+variants in compact form; the full per-kernel detail goes to stderr.
+
+Timing protocol (after the reduce PR's measurement section): warm-up steps,
+then the K timed steps split into 3 trials; before every step a 512 MB
+device buffer is written, which evicts the 4 MB L2s and the 256 MB
+last-level cache, so no step reads its inputs from a cache the previous
+step filled; each step is bracketed by HIP events; the value is the median
+of the 3 trial means of the event span (flush excluded). The CPU oracle is
+timed on bounded samples of the workloads under "cpu_baseline".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -41,21 +51,31 @@ GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", f)
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2,
                     help="index into synthetic.CONFIGS for the main line (default 2: decode T=512)")
     ap.add_argument("--block-m", type=int, default=None)
-    ap.add_argument("--no-t4096", action="store_true", help="skip the T=4096 prefill case")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="device bytes written before every timed step (0 = no flush)")
+    ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--no-t4096", action="store_true",
+                    help="skip the T=4096 prefill, skewed and small workloads")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the standalone reduce and the MFMA probe")
+                    help="skip the standalone reduce, the MFMA probe, the gate and the variants")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512,
+    ap.add_argument("--cpu-tokens", type=int, default=256,
                     help="tokens of the decode workload the oracle runs for the CPU baseline")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated subset of the extra legs to run (t4096, skewed, small, "
+                         "reduce, probe, gate, fp8, w4a8, mx, weighted, w4a8_gemm)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--dump-routing", default=None, metavar="FILE",
                     help="only write the workload's routing (ids, weights) for moe_bench_driver")
+    ap.add_argument("--dump-reduce", default=None, metavar="FILE",
+                    help="only write the skewed workload's standalone-reduce positions and "
+                         "weights for moe_bench_driver")
     return ap.parse_args()
 
 
@@ -83,20 +103,21 @@ def workload_numbers(d, tables_sizes, weights="16bit", weighted_down=False):
     """Algorithmic FLOPs and bytes of one step, per kernel (units in the
     design notes): weights of the experts that receive rows once (FP8: 1
     byte each, W4A8: half a byte, plus a 4-byte scale per row), x read once,
-    h / expert_out written and read once, y written once; W4A8 adds the int8
-    copies of x and h (and their scales), written once and read once."""
+    h / expert_out written and read once, y written once; W4A8 / MX / W8A8
+    add the quantised copies of x and h (and their scales), written once and
+    read once."""
     T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
     b = d["x"].element_size()
-    wb = {"16bit": b, "fp8": 1, "w4a8": 0.5, "mx": 0.5 + 1 / 32}[weights]
-    sc = 4 if weights in ("fp8", "w4a8") else 0   # scale bytes per weight row
+    wb = {"16bit": b, "fp8": 1, "w8a8": 1, "w4a8": 0.5, "mx": 0.5 + 1 / 32}[weights]
+    sc = 4 if weights in ("fp8", "w4a8", "w8a8") else 0   # scale bytes per weight row
     n_valid = int(tables_sizes.sum())
     e_active = int((tables_sizes > 0).sum())
     P = T * K
     w_gate_up = int(e_active * 2 * D * (H * wb + sc))
     w_down = int(e_active * H * (D * wb + sc))
     out = dict(n_valid=n_valid, e_active=e_active)
-    if weights in ("w4a8", "mx"):
-        # int8 + a 4-byte scale per row, or E4M3 + an E8M0 byte per 32 values
+    if weights in ("w4a8", "mx", "w8a8"):
+        # int8 / E4M3 + a 4-byte scale per row, or E4M3 + an E8M0 byte per 32 values
         ab = 1 + 1 / 32 if weights == "mx" else 1
         rs = 0 if weights == "mx" else 4
         out["quant_x_bytes"] = int(T * H * b + T * H * ab + T * rs)
@@ -118,14 +139,73 @@ def workload_numbers(d, tables_sizes, weights="16bit", weighted_down=False):
     return out
 
 
-def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit", weighted_down=False):
-    """One workload's step timed kernel by kernel. weights "fp8" / "w4a8":
-    the expert weights are quantized once (moe_quantize_fp8_rows /
-    moe_quantize_int4_rows, timed on its own, not part of the step) and the
-    step runs the FP8-weight GEMMs, or the W4A8 path (x and h quantised to
-    int8 inside the step, each a timed kernel of its own). weighted_down
-    (16-bit weights): the routing weight applied in the down GEMM's
-    epilogue, then an unweighted reduce."""
+class Flusher:
+    """Writes a `mb`-MB device buffer (a fill kernel on the current stream):
+    more than the 256 MB last-level cache and the L2s, so what a timed call
+    reads next comes from HBM."""
+
+    def __init__(self, dev, mb):
+        import torch
+        self.buf = torch.empty(max(mb, 0) << 20, dtype=torch.uint8, device=dev) if mb > 0 else None
+        self.v = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.v ^= 1
+            self.buf.fill_(self.v)
+
+
+def trial_slices(steps, trials):
+    """Splits `steps` timed steps into `trials` consecutive trials (sizes differ by <= 1)."""
+    trials = max(1, min(trials, steps))
+    sizes = [steps // trials + (1 if i < steps % trials else 0) for i in range(trials)]
+    out, i = [], 0
+    for n in sizes:
+        out.append(slice(i, i + n))
+        i += n
+    return out
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def timed_calls(fn, n_marks, steps, warmup, flush, trials):
+    """Runs fn(events) `warmup` times untimed, then `steps` times, each after
+    flush(); fn records n_marks + 1 events. Returns the median over the
+    trials of the trial means of the span (first to last event) and of each
+    interval between consecutive events, in ms."""
+    import torch
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_marks + 1)]
+    for _ in range(warmup):
+        flush()
+        fn(mk())
+    torch.cuda.synchronize()
+    events = [mk() for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        fn(events[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    spans = [ev[0].elapsed_time(ev[n_marks]) for ev in events]
+    parts = [[ev[j].elapsed_time(ev[j + 1]) for ev in events] for j in range(n_marks)]
+    sl = trial_slices(steps, trials)
+    tmean = lambda v: [sum(v[s]) / (s.stop - s.start) for s in sl]
+    return dict(span=median(tmean(spans)), parts=[median(tmean(p)) for p in parts],
+                trial_spans=[round(x, 4) for x in tmean(spans)], wall_incl_flush=wall)
+
+
+def time_workload(cfg, steps, warmup, block_m, dev, flush, trials, weights="16bit",
+                  weighted_down=False):
+    """One workload's step timed kernel by kernel. weights "fp8" / "w4a8" /
+    "mx" / "w8a8": the expert weights are quantized once (timed on its own,
+    not part of the step) and the step runs that path's GEMMs (W4A8 / MX /
+    W8A8 quantise x and h inside the step, each a timed kernel of its own).
+    weighted_down (16-bit weights): the routing weight applied in the down
+    GEMM's epilogue, then an unweighted reduce."""
     import torch
 
     import mixture_experts_routed_moe_amd as mr
@@ -137,8 +217,8 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit", weighted_do
     t_gen = time.time() - t_gen
     quant_ms = None
     if weights != "16bit":
-        qfn = {"fp8": mr.quantize_fp8_rows, "w4a8": mr.quantize_int4_rows,
-               "mx": mr.quantize_mx_weights}[weights]
+        qfn = {"fp8": mr.quantize_fp8_rows, "w8a8": mr.quantize_fp8_rows,
+               "w4a8": mr.quantize_int4_rows, "mx": mr.quantize_mx_weights}[weights]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
         q = [qfn(d[n]) for n in ("w_gate", "w_up", "w_down")]
@@ -153,12 +233,15 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit", weighted_do
     tables = mr.MoeTables(T, K, E, block_m, dev)
     if weights == "w4a8":
         ws, h, eo, xq, sx, hq, sh = mr.forward_w4a8_workspace(tables, H, D, x.dtype)
-        names = ["dispatch", "quant_x", "gate_up", "quant_h", "down", "reduce"]
     elif weights == "mx":
         ws, h, eo, xq, sx, hq, sh = mr.forward_mx_workspace(tables, H, D, x.dtype)
-        names = ["dispatch", "quant_x", "gate_up", "quant_h", "down", "reduce"]
+    elif weights == "w8a8":
+        ws, h, eo, xq, sx, hq, sh = mr.forward_w8a8_workspace(tables, H, D, x.dtype)
     else:
         ws, h, eo = mr.forward_workspace(tables, H, D, x.dtype)
+    if weights in ("w4a8", "mx", "w8a8"):
+        names = ["dispatch", "quant_x", "gate_up", "quant_h", "down", "reduce"]
+    else:
         names = ["dispatch", "gate_up", "down", "reduce"]
     y = torch.empty(T, H, dtype=x.dtype, device=dev)
     pos = tables.token_topk_to_pos.view(T, K)
@@ -186,6 +269,15 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit", weighted_do
             ev[4].record()
             mr.moe_expert_down_mx(hq, sh, wd, tables, x.dtype, expert_out=eo)
             ev[5].record()
+        elif weights == "w8a8":
+            mr.quantize_fp8_rows(x, q=xq, scales=sx)
+            ev[2].record()
+            mr.moe_expert_gate_up_w8a8(xq, sx, wg, wu, tables, x.dtype, h=h)
+            ev[3].record()
+            mr.quantize_fp8_rows(h, q=hq, scales=sh)
+            ev[4].record()
+            mr.moe_expert_down_w8a8(hq, sh, wd, tables, x.dtype, expert_out=eo)
+            ev[5].record()
         else:
             if weights == "fp8":
                 mr.moe_expert_gate_up_w8(x, wg, wu, tables, h=h)
@@ -202,29 +294,28 @@ def time_workload(cfg, steps, warmup, block_m, dev, weights="16bit", weighted_do
         mr.moe_reduce_fused(eo, pos, None if weighted_down else wt, y=y)
         ev[len(names)].record()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    for _ in range(warmup):
-        step(mk())
-    torch.cuda.synchronize()
-    events = [mk() for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    per = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps
-           for j, n in enumerate(names)}
-    span = sum(ev[0].elapsed_time(ev[len(names)]) for ev in events) / steps
+    t = timed_calls(step, len(names), steps, warmup, flush, trials)
+    per = dict(zip(names, t["parts"]))
     sizes = tables.group_sizes.cpu()
     nums = workload_numbers(d, sizes, weights, weighted_down)
-    return dict(d=d, tables=tables, block_m=block_m, wall_ms=wall_ms, event_ms=span,
-                kernel_ms=per, nums=nums, gen_s=t_gen, quant_ms=quant_ms, weights=weights)
+    return dict(d=d, tables=tables, block_m=block_m, ms=t["span"], trial_ms=t["trial_spans"],
+                wall_incl_flush_ms=t["wall_incl_flush"], kernel_ms=per, nums=nums, gen_s=t_gen,
+                quant_ms=quant_ms, weights=weights, name=cfg["name"], dtype=cfg["dtype"])
+
+
+def mfma_peak(weights, dtype="bf16"):
+    # W4A8 runs int8 MFMA (5.0 POP/s dense), MX the FP8 x FP4 scaled MFMA and
+    # W8A8 the FP8 MFMA (5.0 PFLOP/s); the others bf16 / fp16 MFMA.
+    if dtype == "f32":
+        return 157.3
+    return {"w4a8": MFMA_INT8_PEAK_TOPS, "mx": MFMA_FP8_PEAK_TFLOPS,
+            "w8a8": MFMA_FP8_PEAK_TFLOPS}.get(weights, MFMA_BF16_PEAK_TFLOPS)
 
 
 def summarize(r):
     nums, per = r["nums"], r["kernel_ms"]
-    ms = r["wall_ms"]
+    ms = r["ms"]
+    peak = mfma_peak(r.get("weights"), r.get("dtype", "bf16"))
     gbs = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9
     kernels = {}
     for n in per:
@@ -235,56 +326,66 @@ def summarize(r):
     for n, key in (("gate_up", "flops_gate_up"), ("down", "flops_down")):
         kernels[n]["TFLOP_s" if r.get("weights") != "w4a8" else "TOP_s"] = \
             round(nums[key] / (per[n] * 1e-3) / 1e12, 2)
-    # W4A8 runs int8 MFMA (5.0 POP/s dense), MX the FP8 x FP4 scaled MFMA
-    # (5.0 PFLOP/s at the FP8 rate); the others bf16 / fp16 MFMA
-    peak = {"w4a8": MFMA_INT8_PEAK_TOPS, "mx": MFMA_FP8_PEAK_TFLOPS}.get(r.get("weights"),
-                                                                      MFMA_BF16_PEAK_TFLOPS)
+        t_roof = max(nums[n + "_bytes"] / (HBM_PEAK_GBS * 1e9), nums[key] / (peak * 1e12)) * 1e3
+        kernels[n]["roofline_frac"] = round(t_roof / per[n], 4)
     tflops = nums["flops"] / (ms * 1e-3) / 1e12
     hbm = gbs(nums["b_min"], ms)
     t_roof_ms = max(nums["b_min"] / (HBM_PEAK_GBS * 1e9), nums["flops"] / (peak * 1e12)) * 1e3
-    return dict(ms_per_layer=round(ms, 4), event_ms_per_layer=round(r["event_ms"], 4),
+    return dict(workload=r["name"], ms_per_layer=round(ms, 4), trial_ms=r["trial_ms"],
                 TFLOP_s=round(tflops, 2), HBM_GB_s=round(hbm, 1),
                 hbm_frac=round(hbm / HBM_PEAK_GBS, 4),
                 mfma_frac=round(tflops / peak, 4),
                 roofline_frac=round(t_roof_ms / ms, 4), roofline_ms=round(t_roof_ms, 4),
                 flops=nums["flops"], b_min_bytes=nums["b_min"], n_valid=nums["n_valid"],
-                active_experts=nums["e_active"], block_m=r["block_m"], kernels=kernels)
+                active_experts=nums["e_active"], block_m=r["block_m"], kernels=kernels,
+                quantize_ms=None if r.get("quant_ms") is None else round(r["quant_ms"], 3))
 
 
-def _time_rotating(fn, inputs, steps, warmup):
-    """Average ms of fn(inp) over `steps` calls cycling through `inputs`
-    (copies whose total exceeds the 256 MB last-level cache, so every call
-    reads its rows from HBM)."""
+def compact(s):
+    """The JSON line's short form of a workload summary: ms/layer, fractions
+    of the roofline / HBM / MFMA peaks, and ms and roofline fraction per
+    kernel."""
+    k = s["kernels"]
+    return {"ms": s["ms_per_layer"], "roof": s["roofline_frac"], "hbm": s["hbm_frac"],
+            "mfma": s["mfma_frac"], "TF": s["TFLOP_s"],
+            "k_ms": {n: k[n]["ms"] for n in k},
+            "k_roof": {n: k[n]["roofline_frac"] for n in ("gate_up", "down")}}
+
+
+def run_workload(cfg, args, dev, flush, **kw):
     import torch
-    for i in range(warmup):
-        fn(inputs[i % len(inputs)])
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    ev[0].record()
-    for i in range(steps):
-        fn(inputs[i % len(inputs)])
-    ev[1].record()
-    torch.cuda.synchronize()
-    return ev[0].elapsed_time(ev[1]) / steps
+    r = time_workload(cfg, args.steps, args.warmup, None, dev, flush, args.trials, **kw)
+    r.pop("d")
+    r.pop("tables")
+    torch.cuda.empty_cache()
+    s = summarize(r)
+    print("# %s %s: %.4f ms/layer (trials %s), %.2f TFLOP/s, %.1f GB/s, roofline %.3f"
+          % (cfg["name"], kw, s["ms_per_layer"], s["trial_ms"], s["TFLOP_s"], s["HBM_GB_s"],
+             s["roofline_frac"]), file=sys.stderr, flush=True)
+    return s
 
 
-def time_w4a8_gemm(steps, warmup, dev):
+def time_w4a8_gemm(args, dev, flush):
     """The plain W4A8 GEMM (moe_w4a8_gemm) at the tutorial's two serving
     shapes, N = 3584, K = 18944: M = 1 (a GEMV-like decode step) and M = 32
-    (a small batch). Seeded int8 A and random packed int4 B; 10 copies of B
-    rotate so each call reads its weights from HBM."""
+    (a small batch). Seeded int8 A and random packed int4 B (34 MB, flushed
+    from the caches before every call)."""
     import torch
 
     import mixture_experts_routed_moe_amd as mr
     out = []
     N, K = 3584, 18944
     g = torch.Generator(device=dev).manual_seed(11)
-    Bs = [torch.randint(0, 256, (N, K // 2), generator=g, device=dev, dtype=torch.int16)
-          .to(torch.uint8) for _ in range(10)]
+    B = torch.randint(0, 256, (N, K // 2), generator=g, device=dev, dtype=torch.int16).to(torch.uint8)
     for name, M in (("gemv_like", 1), ("small_batch", 32)):
         A = torch.randint(-127, 128, (M, K), generator=g, device=dev, dtype=torch.int16).to(torch.int8)
         Ct = torch.empty((N, M), dtype=torch.int32, device=dev)
-        ms = _time_rotating(lambda B: mr.w4a8_gemm(A, B, Ct=Ct), Bs, steps, warmup)
+
+        def call(ev):
+            ev[0].record()
+            mr.w4a8_gemm(A, B, Ct=Ct)
+            ev[1].record()
+        ms = timed_calls(call, 1, args.steps, args.warmup, flush, args.trials)["span"]
         nbytes = N * K // 2 + M * K + N * M * 4
         out.append({"workload": "W4A8 GEMM %s M=%d N=%d K=%d" % (name, M, N, K),
                     "us": round(ms * 1e3, 2), "algo_bytes": nbytes,
@@ -293,12 +394,13 @@ def time_w4a8_gemm(steps, warmup, dev):
     return out
 
 
-def time_reduce(steps, warmup, dev):
+def time_reduce(args, dev, flush):
     """The skewed workload's standalone moe_reduce_fused: expert_out [32768,
     7168], 10 % of the slots masked, in bf16 and in the quantized form (FP8
-    E4M3 rows with a scale per row in, FP8 out with a scale per token). Bytes:
-    the valid rows read once, y written once, positions and weights (and the
-    scales) read once."""
+    E4M3 rows with a scale per row in, FP8 out with a scale per token), and
+    the decode-shaped reduce (512 x 8 x 7168 bf16, every slot valid: the
+    reduce PR's headline case). Bytes: the valid rows read once, y written
+    once, positions and weights (and the scales) read once."""
     import torch
 
     import mixture_experts_routed_moe_amd as mr
@@ -310,33 +412,46 @@ def time_reduce(steps, warmup, dev):
     n_valid = int((pos >= 0).sum())
     out = []
 
-    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-    xs = [x, x.clone()]
-    ms = _time_rotating(lambda xi: mr.moe_reduce_fused(xi, pos, w, y=y), xs, steps, warmup)
-    nbytes = n_valid * H * 2 + T * H * 2 + T * K * 8
-    out.append(("skewed standalone reduce 4096x8x7168 bf16, 10% slots masked", ms, nbytes))
-    del xs, y
+    def timed(fn):
+        def call(ev):
+            ev[0].record()
+            fn()
+            ev[1].record()
+        return timed_calls(call, 1, args.steps, args.warmup, flush, args.trials)["span"]
 
-    x8 = [x.to(torch.float8_e4m3fn) for _ in range(3)]
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: mr.moe_reduce_fused(x, pos, w, y=y))
+    out.append(("bf16", "skewed standalone reduce 4096x8x7168 bf16, 10% slots masked", ms,
+                n_valid * H * 2 + T * H * 2 + T * K * 8))
+    del y
+
+    x8 = x.to(torch.float8_e4m3fn)
     del x, d
     g = torch.Generator().manual_seed(cfg["seed"] + 1)
     x_sf = (torch.rand(T * K, generator=g) * 0.05 + 0.01).to(dev)
     sf = (torch.rand(T, generator=g) * 4 + 1).to(dev)
     y8 = torch.empty(T, H, dtype=torch.float8_e4m3fn, device=dev)
-    ms = _time_rotating(lambda xi: mr.moe_reduce_fused(xi, pos, w, y=y8, x_sf=x_sf, sf=sf), x8,
-                        steps, warmup)
-    nbytes = n_valid * H + T * H + T * K * 8 + n_valid * 4 + T * 4
-    out.append(("skewed standalone reduce 4096x8x7168 fp8 e4m3 + x_sf in, fp8 + sf out", ms,
-                nbytes))
-    res = []
-    for name, ms, nbytes in out:
+    ms = timed(lambda: mr.moe_reduce_fused(x8, pos, w, y=y8, x_sf=x_sf, sf=sf))
+    out.append(("fp8", "skewed standalone reduce 4096x8x7168 fp8 e4m3 + x_sf in, fp8 + sf out",
+                ms, n_valid * H + T * H + T * K * 8 + n_valid * 4 + T * 4))
+    del x8, y8
+
+    Td = 512
+    dd = S.make_reduce_inputs(Td, K, H, dtype="bf16", seed=2, mask_frac=0.0, device=dev)
+    yd = torch.empty(Td, H, dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: mr.moe_reduce_fused(dd["expert_out"], dd["token_topk_to_pos"],
+                                           dd["topk_weights"], y=yd))
+    out.append(("decode", "decode-shaped standalone reduce 512x8x7168 bf16", ms,
+                Td * K * H * 2 + Td * H * 2 + Td * K * 8))
+    res = {}
+    for key, name, ms, nbytes in out:
         gbs = nbytes / (ms * 1e-3) / 1e9
-        res.append({"workload": name, "ms": round(ms, 4), "algo_bytes": nbytes,
-                    "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        res[key] = {"workload": name, "us": round(ms * 1e3, 2), "algo_bytes": nbytes,
+                    "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     return res
 
 
-def mfma_probe(steps, warmup, dev):
+def mfma_probe(args, dev, flush):
     """Labelled MFMA probe (not a workload of the metric): the gate/up and
     down kernels on one expert receiving 4096 rows (T=4096, top-1, E=1,
     d_hidden=7168, d_expert=2048): 16 row blocks of 256 share one expert's
@@ -356,16 +471,11 @@ def mfma_probe(steps, warmup, dev):
              4 * 4096 * 7168 * 2048),
             ("down", lambda: mr.moe_expert_down(h, d["w_down"], tables, expert_out=eo),
              2 * 4096 * 7168 * 2048)):
-        for _ in range(warmup):
+        def call(ev, fn=fn):
+            ev[0].record()
             fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for _ in range(steps):
-            fn()
-        ev[1].record()
-        torch.cuda.synchronize()
-        ms = ev[0].elapsed_time(ev[1]) / steps
+            ev[1].record()
+        ms = timed_calls(call, 1, args.steps, args.warmup, flush, args.trials)["span"]
         tf = flops / (ms * 1e-3) / 1e12
         res[name] = {"ms": round(ms, 4), "TFLOP_s": round(tf, 1),
                      "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
@@ -373,7 +483,7 @@ def mfma_probe(steps, warmup, dev):
     return res
 
 
-def time_gate(steps, warmup, dev):
+def time_gate(args, dev, flush):
     """The router gate (moe_gate) at the decode and prefill shapes: logits
     [T, 256] from x [T, 7168] and an fp32 router [256, 7168], top-8, softmax,
     renormalised. An fp32 vector-ALU kernel (one fma chain per logit): FLOPs
@@ -391,22 +501,17 @@ def time_gate(steps, warmup, dev):
         out = (torch.empty(T, K, dtype=torch.int32, device=dev),
                torch.empty(T, K, dtype=torch.float32, device=dev),
                torch.empty(T, E, dtype=torch.float32, device=dev))
-        fn = lambda: mr.moe_gate(d["x"], d["router"], K, renorm=cfg["renorm"], out=out)
-        for _ in range(warmup):
-            fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for _ in range(steps):
-            fn()
-        ev[1].record()
-        torch.cuda.synchronize()
-        ms = ev[0].elapsed_time(ev[1]) / steps
+
+        def call(ev):
+            ev[0].record()
+            mr.moe_gate(d["x"], d["router"], K, renorm=cfg["renorm"], out=out)
+            ev[1].record()
+        ms = timed_calls(call, 1, args.steps, args.warmup, flush, args.trials)["span"]
         flops = 2.0 * T * E * H
         nbytes = T * H * 2 + E * H * 4 + T * E * 4 + T * K * 8
         tf = flops / (ms * 1e-3) / 1e12
-        res.append({"workload": "router gate, %s (T=%d, E=%d, H=%d, top-%d)" % (cfg["name"], T, E,
-                                                                               H, K),
+        res.append({"workload": "router gate, %s (T=%d, E=%d, H=%d, top-%d)"
+                                % (cfg["name"], T, E, H, K),
                     "us": round(ms * 1e3, 2), "TFLOP_s": round(tf, 2),
                     "fp32_vector_frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
                     "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
@@ -414,42 +519,90 @@ def time_gate(steps, warmup, dev):
     return res
 
 
-def cpu_baseline(r, n_tokens):
-    """The oracle (as it stands) on the first n_tokens tokens of the workload,
-    plus its dispatch of the whole batch; time scaled to the whole layer."""
+def host_info():
+    """nproc (usable and online), the CPU model and the socket count of this host."""
+    model, sockets = None, set()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name") and model is None:
+                model = line.split(":", 1)[1].strip()
+            elif line.startswith("physical id"):
+                sockets.add(line.split(":", 1)[1].strip())
+    except OSError:
+        pass
+    return {"nproc": len(os.sched_getaffinity(0)), "cpus_online": os.cpu_count(),
+            "cpu_model": model, "sockets": len(sockets) or None}
+
+
+def oracle_forward_seconds(cfg, n_tokens, threads=None):
+    """Seconds the oracle takes for the dispatch of the whole batch plus the
+    forward of its first n_tokens tokens (inputs generated on the host
+    first; generation is not timed), and the token count used."""
     import numpy as np
     import torch
 
     import oracle
-
-    d = r["d"]
-    T, K, E = d["T"], d["K"], d["E"]
-    n_tokens = min(n_tokens, T)
-    tokens = np.arange(n_tokens, dtype=np.int32)
-    ids = d["topk_ids"].cpu().numpy()
-    w = d["topk_weights"].cpu().numpy()
-    sub = ids[:n_tokens]
+    import synthetic as S
+    d = S.make_moe_inputs(cfg, device="cpu")
+    T, K, E = cfg["T"], cfg["K"], cfg["E"]
+    n = min(n_tokens, T)
+    ids = d["topk_ids"].numpy()
+    w = d["topk_weights"].numpy()
+    sub = ids[:n]
     used = np.unique(sub[sub >= 0])
     remap = np.full(E, -1, np.int32)
     remap[used] = np.arange(used.size, dtype=np.int32)
     sub_ids = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
-    sel = torch.from_numpy(used).long().to(d["x"].device)
-    bits = lambda t: t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
-    xs, gs, us, ds = (bits(d["x"][:n_tokens]), bits(d["w_gate"][sel]), bits(d["w_up"][sel]),
-                      bits(d["w_down"][sel]))
-    t0 = time.perf_counter()
-    oracle.dispatch(ids, w, E, r["block_m"])
-    t_disp = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.moe_forward(oracle.BF16, xs, gs, us, ds, sub_ids, w[:n_tokens], tokens=tokens)
-    t_fwd = time.perf_counter() - t0
-    ms = (t_disp + t_fwd * T / n_tokens) * 1e3
-    return {"value": round(ms, 1), "unit": "ms/layer", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "oracle forward on %d of %d tokens (%d routed pairs, %.1f s) scaled by "
-                      "T/%d, plus its dispatch of all %d pairs (%.3f s); same seeded "
-                      "decode workload" % (n_tokens, T, n_tokens * K, t_fwd, n_tokens, T * K,
-                                           t_disp)}
+    sel = torch.from_numpy(used).long()
+    if cfg["dtype"] == "f32":
+        st, dt = (lambda t: t.contiguous().numpy()), oracle.F32
+    else:
+        st = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+        dt = oracle.BF16 if cfg["dtype"] == "bf16" else oracle.F16
+    args = (st(d["x"][:n]), st(d["w_gate"][sel]), st(d["w_up"][sel]), st(d["w_down"][sel]))
+    del d
+    prev = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    try:
+        t0 = time.perf_counter()
+        oracle.dispatch(ids, w, E, 32)
+        oracle.moe_forward(dt, *args, sub_ids, w[:n], tokens=np.arange(n, dtype=np.int32))
+        sec = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(prev)
+    return sec, n
+
+
+def cpu_baseline(args):
+    """The oracle (as it stands) on bounded samples: the decode workload's
+    first --cpu-tokens tokens (the reported value, scaled to the layer), the
+    tiny workload whole and the mid-size one on 64 tokens at all threads and
+    at 1 thread, and the two T = 4096 workloads on 24 tokens."""
+    import oracle
+    import synthetic as S
+    threads = oracle.num_threads()
+    per = {}
+    main = None
+    for ci, n_tok, one in ((2, args.cpu_tokens, False), (0, 64, True), (1, 64, True),
+                           (3, 24, False), (4, 24, False)):
+        cfg = S.CONFIGS[ci]
+        sec, n = oracle_forward_seconds(cfg, n_tok)
+        ms = sec * 1e3 * cfg["T"] / n
+        e = {"ms_layer": round(ms, 1), "tokens": n}
+        if one:
+            sec1, _ = oracle_forward_seconds(cfg, n_tok, threads=1)
+            e["ms_layer_1thread"] = round(sec1 * 1e3 * cfg["T"] / n, 1)
+        per[cfg["name"]] = e
+        if ci == 2:
+            main = (ms, n, sec)
+        print("# cpu oracle %s: %s" % (cfg["name"], e), file=sys.stderr, flush=True)
+    ms, n, sec = main
+    return {"value": round(ms, 1), "unit": "ms/layer", "cores": threads, "kind": "oracle",
+            "sample": "oracle dispatch of all 4096 pairs + forward of %d of 512 tokens of the "
+                      "seeded decode workload (%.1f s), scaled by 512/%d; per_config: the other "
+                      "workloads on the token counts given, also scaled to a layer" % (n, sec, n),
+            "host": host_info(), "per_config": per}
 
 
 def dump_routing(cfg, block_m, path):
@@ -469,6 +622,23 @@ def dump_routing(cfg, block_m, path):
         f.write(d["topk_ids"].numpy().astype(np.int32).tobytes())
         f.write(d["topk_weights"].numpy().astype(np.float32).tobytes())
     print(json.dumps({"routing_dump": path, "workload": cfg["name"], "block_m": int(block_m)}))
+
+
+def dump_reduce(path):
+    """Write {magic, T, K, H} + positions + weights of the skewed workload's
+    standalone reduce for the C++ driver (moe_bench_driver reduce FILE)."""
+    import numpy as np
+
+    import synthetic as S
+    cfg = S.CONFIGS[4]
+    T, K, H = cfg["T"], cfg["K"], cfg["H"]
+    d = S.make_reduce_inputs(T, K, H, dtype="bf16", seed=cfg["seed"], device="cpu", rows=False)
+    hdr = np.array([0x4d6f4532, T, K, H], np.int32)
+    with open(path, "wb") as f:
+        f.write(hdr.tobytes())
+        f.write(d["token_topk_to_pos"].numpy().astype(np.int32).tobytes())
+        f.write(d["topk_weights"].numpy().astype(np.float32).tobytes())
+    print(json.dumps({"reduce_dump": path, "T": T, "K": K, "H": H}))
 
 
 def copy_calibration(dev):
@@ -494,97 +664,78 @@ def main():
     if args.dump_routing:
         dump_routing(S.CONFIGS[args.workload], args.block_m, args.dump_routing)
         return
+    if args.dump_reduce:
+        dump_reduce(args.dump_reduce)
+        return
     import torch
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(dev)
         return
+    legs = set(args.only.split(",")) if args.only else None
+    want = lambda leg: legs is None or leg in legs
+    flush = Flusher(dev, args.flush_mb)
 
     cfg = S.CONFIGS[args.workload]
-    main_r = time_workload(cfg, args.steps, args.warmup, args.block_m, dev)
+    main_r = time_workload(cfg, args.steps, args.warmup, args.block_m, dev, flush, args.trials)
     main_s = summarize(main_r)
-    print("# %s: %.4f ms/layer, %.1f GB/s (%.1f%% of HBM peak), gen %.1fs"
-          % (cfg["name"], main_s["ms_per_layer"], main_s["HBM_GB_s"], 100 * main_s["hbm_frac"],
-             main_r["gen_s"]), file=sys.stderr, flush=True)
+    print("# %s: %.4f ms/layer (trials %s), %.1f GB/s (%.1f%% of HBM peak), gen %.1fs"
+          % (cfg["name"], main_s["ms_per_layer"], main_s["trial_ms"], main_s["HBM_GB_s"],
+             100 * main_s["hbm_frac"], main_r["gen_s"]), file=sys.stderr, flush=True)
+    print("# main detail: %s" % json.dumps(main_s), file=sys.stderr, flush=True)
+    del main_r["d"], main_r["tables"]
+    torch.cuda.empty_cache()
+
+    tail = {}          # compact entries, printed last in the JSON line
+    detail = {}
+    if not args.no_t4096 and args.workload == 2:
+        for key, ci in (("tiny", 0), ("mid", 1), ("t4096", 3), ("skewed", 4)):
+            if key in ("tiny", "mid") and not want("small"):
+                continue
+            if key in ("t4096", "skewed") and not want(key):
+                continue
+            s = run_workload(S.CONFIGS[ci], args, dev, flush)
+            detail[key] = s
+            tail[key] = dict(compact(s), n_act=s["active_experts"])
+    extras = {}
+    variants = {}
+    if not args.no_extras:
+        if want("reduce"):
+            extras["reduce_skewed"] = time_reduce(args, dev, flush)
+            torch.cuda.empty_cache()
+            tail["reduce_skewed"] = {k: {"us": v["us"], "hbm": v["hbm_frac"]}
+                                     for k, v in extras["reduce_skewed"].items()}
+        if want("probe"):
+            extras["mfma_probe"] = mfma_probe(args, dev, flush)
+            torch.cuda.empty_cache()
+            tail["mfma_probe"] = {k: extras["mfma_probe"][k]["mfma_frac"] for k in ("gate_up", "down")}
+        if want("gate"):
+            extras["gate"] = time_gate(args, dev, flush)
+            torch.cuda.empty_cache()
+        for leg, kw in (("fp8", dict(weights="fp8")), ("w8a8", dict(weights="w8a8")),
+                        ("w4a8", dict(weights="w4a8")), ("mx", dict(weights="mx")),
+                        ("weighted", dict(weighted_down=True))):
+            if not want(leg):
+                continue
+            if leg == "w8a8" and not hasattr(__import__("mixture_experts_routed_moe_amd"),
+                                             "moe_expert_gate_up_w8a8"):
+                continue
+            for ci in (2, 3):
+                s = run_workload(S.CONFIGS[ci], args, dev, flush, **kw)
+                extras.setdefault(leg, {})["T%d" % S.CONFIGS[ci]["T"]] = s
+                variants["%s_T%d" % (leg, S.CONFIGS[ci]["T"])] = [s["ms_per_layer"],
+                                                                  s["roofline_frac"]]
+        if want("w4a8_gemm"):
+            extras["w4a8_gemm"] = time_w4a8_gemm(args, dev, flush)
+            torch.cuda.empty_cache()
+        print("# extras: %s" % json.dumps(extras), file=sys.stderr, flush=True)
+    if detail:
+        print("# workloads: %s" % json.dumps(detail), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(main_r, args.cpu_tokens)
+        cpu = cpu_baseline(args)
         print("# cpu baseline: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
-    main_d = main_r.pop("d")
-    del main_d, main_r["tables"]
-    torch.cuda.empty_cache()
-
-    t4096 = None
-    if not args.no_t4096 and args.workload == 2:
-        r3 = time_workload(S.CONFIGS[3], args.steps, args.warmup, None, dev)
-        r3.pop("d")
-        r3.pop("tables")
-        torch.cuda.empty_cache()
-        t4096 = summarize(r3)
-        t4096["workload"] = S.CONFIGS[3]["name"]
-        print("# %s: %.4f ms/layer, %.2f TFLOP/s, %.1f GB/s"
-              % (S.CONFIGS[3]["name"], t4096["ms_per_layer"], t4096["TFLOP_s"],
-                 t4096["HBM_GB_s"]), file=sys.stderr, flush=True)
-
-    extras = {}
-    if not args.no_extras:
-        extras["reduce_skewed"] = time_reduce(args.steps, args.warmup, dev)
-        torch.cuda.empty_cache()
-        extras["mfma_probe"] = mfma_probe(args.steps, args.warmup, dev)
-        torch.cuda.empty_cache()
-        extras["gate"] = time_gate(args.steps, args.warmup, dev)
-        torch.cuda.empty_cache()
-        fp8 = {}
-        for ci in (2, 3):
-            r8 = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev, weights="fp8")
-            r8.pop("d")
-            r8.pop("tables")
-            torch.cuda.empty_cache()
-            s8 = summarize(r8)
-            s8["quantize_ms"] = round(r8["quant_ms"], 3)
-            s8["workload"] = S.CONFIGS[ci]["name"] + " with FP8 E4M3 expert weights (per-row scales)"
-            fp8["T%d" % S.CONFIGS[ci]["T"]] = s8
-        extras["fp8_weights"] = fp8
-        w4 = {}
-        for ci in (2, 3):
-            r4 = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev, weights="w4a8")
-            r4.pop("d")
-            r4.pop("tables")
-            torch.cuda.empty_cache()
-            s4 = summarize(r4)
-            s4["quantize_ms"] = round(r4["quant_ms"], 3)
-            s4["workload"] = (S.CONFIGS[ci]["name"] + " with W4A8 experts (int4 weights, per-row "
-                              "scales; int8 activations, per-row scales)")
-            w4["T%d" % S.CONFIGS[ci]["T"]] = s4
-        extras["w4a8"] = w4
-        mx = {}
-        for ci in (2, 3):
-            rm = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev, weights="mx")
-            rm.pop("d")
-            rm.pop("tables")
-            torch.cuda.empty_cache()
-            sm = summarize(rm)
-            sm["quantize_ms"] = round(rm["quant_ms"], 3)
-            sm["workload"] = (S.CONFIGS[ci]["name"] + " with MX experts (MXFP4 weights, MXFP8 "
-                              "activations, E8M0 scales per 32 values)")
-            mx["T%d" % S.CONFIGS[ci]["T"]] = sm
-        extras["mx"] = mx
-        wdn = {}
-        for ci in (2, 3):
-            rw = time_workload(S.CONFIGS[ci], args.steps, args.warmup, None, dev,
-                               weighted_down=True)
-            rw.pop("d")
-            rw.pop("tables")
-            torch.cuda.empty_cache()
-            sw = summarize(rw)
-            sw["workload"] = (S.CONFIGS[ci]["name"] + " with the routing weight in the down "
-                              "epilogue and an unweighted reduce")
-            wdn["T%d" % S.CONFIGS[ci]["T"]] = sw
-        extras["weighted_down"] = wdn
-        extras["w4a8_gemm"] = time_w4a8_gemm(args.steps, args.warmup, dev)
-        torch.cuda.empty_cache()
-        print("# %s" % json.dumps(extras), file=sys.stderr, flush=True)
 
     gu = main_s["kernels"]["gate_up"]
     achieved = gu["GB_s"]
@@ -602,26 +753,24 @@ def main():
         "config": {"workload": cfg["name"], "T": cfg["T"], "d_hidden": cfg["H"],
                    "d_expert": cfg["D"], "n_routed_experts": cfg["E"], "top_k": cfg["K"],
                    "block_m": main_s["block_m"]},
-        "TFLOP_s": main_s["TFLOP_s"], "HBM_GB_s": main_s["HBM_GB_s"],
-        "hbm_frac": main_s["hbm_frac"], "mfma_frac": main_s["mfma_frac"],
-        "roofline_frac": main_s["roofline_frac"],
         "roofline": {"bound": "hbm", "kernel": "grouped_gemm gate/up (SiLU*up fused)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algo_bytes_per_launch": gu["algo_bytes"],
                      "avg_launch_ms": gu["ms"]},
-        "kernels": main_s["kernels"],
-        "t4096": t4096,
-        "reduce_skewed": extras.get("reduce_skewed"),
-        "mfma_probe": extras.get("mfma_probe"),
-        "gate": extras.get("gate"),
-        "fp8_weights": extras.get("fp8_weights"),
-        "w4a8": extras.get("w4a8"),
-        "w4a8_gemm": extras.get("w4a8_gemm"),
-        "weighted_down": extras.get("weighted_down"),
-        "mx": extras.get("mx"),
         "cpu_baseline": cpu,
+        "protocol": "%d trials x ~%d steps, median of trial means; %d MB flush before each "
+                    "step" % (args.trials, max(1, args.steps // max(1, args.trials)),
+                              args.flush_mb),
+        "TFLOP_s": main_s["TFLOP_s"], "HBM_GB_s": main_s["HBM_GB_s"],
+        "hbm_frac": main_s["hbm_frac"], "mfma_frac": main_s["mfma_frac"],
+        "roofline_frac": main_s["roofline_frac"],
+        "kernels": {n: [k["ms"], k["hbm_frac"]] for n, k in main_s["kernels"].items()},
+        "variants": variants or None,
     }
+    for key in ("tiny", "mid", "mfma_probe", "reduce_skewed", "skewed", "t4096"):
+        if key in tail:
+            line[key] = tail[key]
     print(json.dumps(line), flush=True)
 
 

@@ -2,14 +2,24 @@
 // Python or torch in the process (for hardware-counter profiler passes, and as
 // a usage example of the ABI).
 //
-//   moe_bench_driver routing FILE [STEPS]
+//   moe_bench_driver routing FILE [STEPS] [FORMAT]
 //       Replays a routing dump written by `bench.py --dump-routing FILE`:
 //       header {magic, T, K, E, H, D, dtype, block_m} (int32) then topk_ids
 //       int32 [T*K] and topk_weights fp32 [T*K]. x and the stacked expert
 //       weights are filled on the device with a hashed pattern of the right
 //       scale (the data values do not change the memory traffic), then
-//       moe_dispatch + moe_routed_forward run STEPS times; per-step times
-//       from HIP events are printed.
+//       moe_dispatch + the forward run STEPS times; per-step times from HIP
+//       events are printed. FORMAT selects the forward: 16bit (default,
+//       moe_routed_forward), weighted (moe_routed_forward_weighted), fp8
+//       (FP8 weights, moe_routed_forward_w8), w4a8 (moe_routed_forward_w4a8)
+//       or mx (moe_routed_forward_mx); the weights are quantised once with
+//       the library's quantizers before the steps.
+//   moe_bench_driver reduce FILE [STEPS] [bf16|fp8]
+//       The standalone moe_reduce_fused of a dump written by `bench.py
+//       --dump-reduce FILE`: header {magic, T, K, H} then token_topk_to_pos
+//       int32 [T*K] and topk_weights fp32 [T*K]; expert_out [T*K, H] is
+//       filled with a hashed pattern (bf16, or FP8 E4M3 codes with a scale
+//       per row and per token: the quantized form).
 //   moe_bench_driver copy BYTES [STEPS]
 //       A plain 16-byte-per-lane device copy of BYTES bytes (calibrates the
 //       FETCH_SIZE / WRITE_SIZE counters against a known transfer).
@@ -27,7 +37,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int32_t kMagic = 0x4d6f4531;   // "MoE1"
+constexpr int32_t kMagic = 0x4d6f4531;        // "MoE1": routing dump
+constexpr int32_t kMagicReduce = 0x4d6f4532;  // "MoE2": standalone-reduce dump
 
 #define CHECK_HIP(x)                                                                  \
   do {                                                                                \
@@ -64,6 +75,25 @@ __global__ void fill_kernel(uint16_t* p, size_t n, uint32_t seed, float scale, i
       bits = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
     }
     p[i] = bits;
+  }
+}
+
+// Hashed FP8 E4M3 codes of magnitude <= 1.75 (exponent field <= 7), signed.
+__global__ void fill_fp8_kernel(uint8_t* p, size_t n, uint32_t seed) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    uint32_t h = static_cast<uint32_t>(i) * 2654435761u ^ seed;
+    h ^= h >> 16;
+    h *= 0x7feb352du;
+    h ^= h >> 15;
+    p[i] = static_cast<uint8_t>((h & 0x80u) | ((h >> 8) & 0x3fu));
+  }
+}
+
+__global__ void fill_f32_kernel(float* p, size_t n, float v) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    p[i] = v;
   }
 }
 
@@ -105,7 +135,24 @@ int run_copy(size_t bytes, int steps) {
   return 0;
 }
 
-int run_routing(const char* path, int steps) {
+enum Format { kFmt16 = 0, kFmtWeighted, kFmtFp8, kFmtW4a8, kFmtMx };
+
+int parse_format(const char* s) {
+  if (!s || std::strcmp(s, "16bit") == 0) return kFmt16;
+  if (std::strcmp(s, "weighted") == 0) return kFmtWeighted;
+  if (std::strcmp(s, "fp8") == 0) return kFmtFp8;
+  if (std::strcmp(s, "w4a8") == 0) return kFmtW4a8;
+  if (std::strcmp(s, "mx") == 0) return kFmtMx;
+  return -1;
+}
+
+void* dmalloc(size_t bytes) {
+  void* p = nullptr;
+  CHECK_HIP(hipMalloc(&p, bytes ? bytes : 1));
+  return p;
+}
+
+int run_routing(const char* path, int steps, int fmt) {
   FILE* f = std::fopen(path, "rb");
   if (!f) {
     std::fprintf(stderr, "cannot open %s\n", path);
@@ -129,59 +176,195 @@ int run_routing(const char* path, int steps) {
     std::fprintf(stderr, "%s is truncated\n", path);
     return 1;
   }
-  std::printf("routing %s: T=%d K=%d E=%d H=%d D=%d dtype=%d block_m=%d\n", path, T, K, E, H,
-              D, dtype, block_m);
+  if (fmt != kFmt16 && fmt != kFmtWeighted && dtype == MOE_F32) {
+    std::fprintf(stderr, "quantised formats need a 16-bit dtype\n");
+    return 1;
+  }
+  std::printf("routing %s: T=%d K=%d E=%d H=%d D=%d dtype=%d block_m=%d format=%d\n", path, T, K,
+              E, H, D, dtype, block_m, fmt);
 
-  int32_t* d_ids = nullptr;
-  float* d_w = nullptr;
-  CHECK_HIP(hipMalloc(&d_ids, P * sizeof(int32_t)));
-  CHECK_HIP(hipMalloc(&d_w, P * sizeof(float)));
+  int32_t* d_ids = static_cast<int32_t*>(dmalloc(P * sizeof(int32_t)));
+  float* d_w = static_cast<float*>(dmalloc(P * sizeof(float)));
   CHECK_HIP(hipMemcpy(d_ids, ids.data(), P * sizeof(int32_t), hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(d_w, w.data(), P * sizeof(float), hipMemcpyHostToDevice));
 
   const size_t nx = static_cast<size_t>(T) * H;
   const size_t nw = static_cast<size_t>(E) * D * H;
-  uint16_t *x = nullptr, *wg = nullptr, *wu = nullptr, *wd = nullptr, *y = nullptr;
-  CHECK_HIP(hipMalloc(&x, nx * 2));
-  CHECK_HIP(hipMalloc(&wg, nw * 2));
-  CHECK_HIP(hipMalloc(&wu, nw * 2));
-  CHECK_HIP(hipMalloc(&wd, nw * 2));
-  CHECK_HIP(hipMalloc(&y, nx * 2));
+  uint16_t* x = static_cast<uint16_t*>(dmalloc(nx * 2));
+  uint16_t* y = static_cast<uint16_t*>(dmalloc(nx * 2));
+  uint16_t* wt[3];
+  for (auto& p : wt) p = static_cast<uint16_t*>(dmalloc(nw * 2));
   fill(x, nx, 1, 1.7f, dtype);
-  fill(wg, nw, 2, 1.7f / std::sqrt(static_cast<float>(H)), dtype);
-  fill(wu, nw, 3, 1.7f / std::sqrt(static_cast<float>(H)), dtype);
-  fill(wd, nw, 4, 1.7f / std::sqrt(static_cast<float>(D)), dtype);
+  fill(wt[0], nw, 2, 1.7f / std::sqrt(static_cast<float>(H)), dtype);
+  fill(wt[1], nw, 3, 1.7f / std::sqrt(static_cast<float>(H)), dtype);
+  fill(wt[2], nw, 4, 1.7f / std::sqrt(static_cast<float>(D)), dtype);
+
+  // Quantised weights: codes and scales from the library's quantizers; the
+  // 16-bit copies are freed before the steps.
+  void* q[3] = {nullptr, nullptr, nullptr};
+  void* s[3] = {nullptr, nullptr, nullptr};
+  const int64_t rows[3] = {static_cast<int64_t>(E) * D, static_cast<int64_t>(E) * D,
+                           static_cast<int64_t>(E) * H};
+  const int cols[3] = {H, H, D};
+  if (fmt == kFmtFp8 || fmt == kFmtW4a8 || fmt == kFmtMx) {
+    for (int i = 0; i < 3; ++i) {
+      const size_t n = static_cast<size_t>(rows[i]) * cols[i];
+      if (fmt == kFmtFp8) {
+        q[i] = dmalloc(n);
+        s[i] = dmalloc(rows[i] * sizeof(float));
+        CHECK_MOE(moe_quantize_fp8_rows(wt[i], rows[i], cols[i], dtype, static_cast<uint8_t*>(q[i]),
+                                        static_cast<float*>(s[i]), nullptr));
+      } else if (fmt == kFmtW4a8) {
+        q[i] = dmalloc(n / 2);
+        s[i] = dmalloc(rows[i] * sizeof(float));
+        CHECK_MOE(moe_quantize_int4_rows(wt[i], rows[i], cols[i], dtype,
+                                         static_cast<uint8_t*>(q[i]), static_cast<float*>(s[i]),
+                                         nullptr));
+      } else {
+        q[i] = dmalloc(n / 2);
+        s[i] = dmalloc(n / 32);
+        CHECK_MOE(moe_quantize_mx_rows(wt[i], rows[i], cols[i], dtype, MOE_MX_FP4,
+                                       static_cast<uint8_t*>(q[i]), static_cast<uint8_t*>(s[i]),
+                                       nullptr));
+      }
+    }
+    CHECK_HIP(hipDeviceSynchronize());
+    for (auto& p : wt) {
+      CHECK_HIP(hipFree(p));
+      p = nullptr;
+    }
+  }
 
   const size_t tb = moe_tables_bytes(T, K, E, block_m);
-  void* tbuf = nullptr;
-  CHECK_HIP(hipMalloc(&tbuf, tb));
+  void* tbuf = dmalloc(tb);
   moe_tables tables;
   CHECK_MOE(moe_tables_bind(&tables, tbuf, tb, T, K, E, block_m));
-  const size_t wsb = moe_forward_workspace_bytes(T, K, H, D, dtype);
-  void* ws = nullptr;
-  CHECK_HIP(hipMalloc(&ws, wsb));
+  size_t wsb = moe_forward_workspace_bytes(T, K, H, D, dtype);
+  if (fmt == kFmtW4a8) wsb = moe_forward_w4a8_workspace_bytes(T, K, H, D, dtype);
+  if (fmt == kFmtMx) wsb = moe_forward_mx_workspace_bytes(T, K, H, D, dtype);
+  void* ws = dmalloc(wsb);
   CHECK_HIP(hipDeviceSynchronize());
 
+  const uint8_t* const* qb = reinterpret_cast<const uint8_t* const*>(q);
   hipEvent_t ev[3];
   for (auto& e : ev) CHECK_HIP(hipEventCreate(&e));
-  for (int s = 0; s < steps; ++s) {
+  for (int st = 0; st < steps; ++st) {
     CHECK_HIP(hipEventRecord(ev[0], nullptr));
     CHECK_MOE(moe_dispatch(d_ids, d_w, &tables, nullptr));
     CHECK_HIP(hipEventRecord(ev[1], nullptr));
-    CHECK_MOE(moe_routed_forward(x, wg, wu, wd, &tables, H, D, dtype, ws, wsb, y, nullptr));
+    switch (fmt) {
+      case kFmt16:
+        CHECK_MOE(moe_routed_forward(x, wt[0], wt[1], wt[2], &tables, H, D, dtype, ws, wsb, y,
+                                     nullptr));
+        break;
+      case kFmtWeighted:
+        CHECK_MOE(moe_routed_forward_weighted(x, wt[0], wt[1], wt[2], &tables, H, D, dtype, ws,
+                                              wsb, y, nullptr));
+        break;
+      case kFmtFp8:
+        CHECK_MOE(moe_routed_forward_w8(x, qb[0], qb[1], qb[2], static_cast<float*>(s[0]),
+                                        static_cast<float*>(s[1]), static_cast<float*>(s[2]),
+                                        &tables, H, D, dtype, ws, wsb, y, nullptr));
+        break;
+      case kFmtW4a8:
+        CHECK_MOE(moe_routed_forward_w4a8(x, qb[0], qb[1], qb[2], static_cast<float*>(s[0]),
+                                          static_cast<float*>(s[1]), static_cast<float*>(s[2]),
+                                          &tables, H, D, dtype, ws, wsb, y, nullptr));
+        break;
+      default:
+        CHECK_MOE(moe_routed_forward_mx(x, qb[0], qb[1], qb[2], static_cast<uint8_t*>(s[0]),
+                                        static_cast<uint8_t*>(s[1]), static_cast<uint8_t*>(s[2]),
+                                        &tables, H, D, dtype, ws, wsb, y, nullptr));
+        break;
+    }
     CHECK_HIP(hipEventRecord(ev[2], nullptr));
     CHECK_HIP(hipEventSynchronize(ev[2]));
     float ms_d = 0.0f, ms_f = 0.0f;
     CHECK_HIP(hipEventElapsedTime(&ms_d, ev[0], ev[1]));
     CHECK_HIP(hipEventElapsedTime(&ms_f, ev[1], ev[2]));
-    std::printf("step %d: dispatch %.4f ms, forward %.4f ms\n", s, ms_d, ms_f);
+    std::printf("step %d: dispatch %.4f ms, forward %.4f ms\n", st, ms_d, ms_f);
   }
   int32_t status = 0;
   CHECK_HIP(hipMemcpy(&status, tables.status, sizeof(int32_t), hipMemcpyDeviceToHost));
   std::printf("dispatch status %d\n", status);
   for (void* p : {static_cast<void*>(d_ids), static_cast<void*>(d_w), static_cast<void*>(x),
-                  static_cast<void*>(wg), static_cast<void*>(wu), static_cast<void*>(wd),
-                  static_cast<void*>(y), tbuf, ws}) {
+                  static_cast<void*>(y), tbuf, ws, static_cast<void*>(wt[0]),
+                  static_cast<void*>(wt[1]), static_cast<void*>(wt[2]), q[0], q[1], q[2], s[0],
+                  s[1], s[2]}) {
+    if (p) CHECK_HIP(hipFree(p));
+  }
+  return 0;
+}
+
+int run_reduce(const char* path, int steps, bool fp8) {
+  FILE* f = std::fopen(path, "rb");
+  if (!f) {
+    std::fprintf(stderr, "cannot open %s\n", path);
+    return 1;
+  }
+  int32_t hdr[4];
+  if (std::fread(hdr, sizeof(int32_t), 4, f) != 4 || hdr[0] != kMagicReduce) {
+    std::fprintf(stderr, "%s is not a reduce dump\n", path);
+    std::fclose(f);
+    return 1;
+  }
+  const int T = hdr[1], K = hdr[2], H = hdr[3];
+  const size_t P = static_cast<size_t>(T) * K;
+  std::vector<int32_t> pos(P);
+  std::vector<float> w(P);
+  const bool ok = std::fread(pos.data(), sizeof(int32_t), P, f) == P &&
+                  std::fread(w.data(), sizeof(float), P, f) == P;
+  std::fclose(f);
+  if (!ok) {
+    std::fprintf(stderr, "%s is truncated\n", path);
+    return 1;
+  }
+  for (int32_t p : pos) {
+    if (p >= static_cast<int64_t>(P)) {
+      std::fprintf(stderr, "%s holds a position out of range\n", path);
+      return 1;
+    }
+  }
+  std::printf("reduce %s: T=%d K=%d H=%d %s\n", path, T, K, H, fp8 ? "fp8" : "bf16");
+  int32_t* d_pos = static_cast<int32_t*>(dmalloc(P * sizeof(int32_t)));
+  float* d_w = static_cast<float*>(dmalloc(P * sizeof(float)));
+  CHECK_HIP(hipMemcpy(d_pos, pos.data(), P * sizeof(int32_t), hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(d_w, w.data(), P * sizeof(float), hipMemcpyHostToDevice));
+  const size_t n = P * H;
+  void* xo = dmalloc(n * (fp8 ? 1 : 2));
+  void* y = dmalloc(static_cast<size_t>(T) * H * (fp8 ? 1 : 2));
+  float* x_sf = static_cast<float*>(dmalloc(P * sizeof(float)));
+  float* sf = static_cast<float*>(dmalloc(T * sizeof(float)));
+  if (fp8) {
+    hipLaunchKernelGGL(fill_fp8_kernel, dim3(8192), dim3(256), 0, nullptr,
+                       static_cast<uint8_t*>(xo), n, 5u);
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(256), dim3(256), 0, nullptr, x_sf, P, 0.03f);
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(16), dim3(256), 0, nullptr, sf, static_cast<size_t>(T),
+                       2.0f);
+    CHECK_HIP(hipGetLastError());
+  } else {
+    fill(static_cast<uint16_t*>(xo), n, 5, 1.7f, MOE_BF16);
+  }
+  CHECK_HIP(hipDeviceSynchronize());
+  hipEvent_t ev[2];
+  for (auto& e : ev) CHECK_HIP(hipEventCreate(&e));
+  for (int st = 0; st < steps; ++st) {
+    CHECK_HIP(hipEventRecord(ev[0], nullptr));
+    if (fp8) {
+      CHECK_MOE(moe_reduce_fused_scaled(xo, static_cast<int64_t>(P), d_pos, d_w, x_sf, sf, T, K, H,
+                                        MOE_FP8_E4M3, MOE_FP8_E4M3, y, nullptr));
+    } else {
+      CHECK_MOE(moe_reduce_fused(xo, static_cast<int64_t>(P), d_pos, d_w, T, K, H, MOE_BF16,
+                                 MOE_BF16, y, nullptr));
+    }
+    CHECK_HIP(hipEventRecord(ev[1], nullptr));
+    CHECK_HIP(hipEventSynchronize(ev[1]));
+    float ms = 0.0f;
+    CHECK_HIP(hipEventElapsedTime(&ms, ev[0], ev[1]));
+    std::printf("step %d: reduce %.4f ms\n", st, ms);
+  }
+  for (void* p : {static_cast<void*>(d_pos), static_cast<void*>(d_w), xo, y,
+                  static_cast<void*>(x_sf), static_cast<void*>(sf)}) {
     CHECK_HIP(hipFree(p));
   }
   return 0;
@@ -191,11 +374,23 @@ int run_routing(const char* path, int steps) {
 
 int main(int argc, char** argv) {
   if (argc >= 3 && std::strcmp(argv[1], "routing") == 0) {
-    return run_routing(argv[2], argc >= 4 ? std::atoi(argv[3]) : 3);
+    const int fmt = parse_format(argc >= 5 ? argv[4] : nullptr);
+    if (fmt < 0) {
+      std::fprintf(stderr, "unknown format %s\n", argv[4]);
+      return 1;
+    }
+    return run_routing(argv[2], argc >= 4 ? std::atoi(argv[3]) : 3, fmt);
+  }
+  if (argc >= 3 && std::strcmp(argv[1], "reduce") == 0) {
+    const bool fp8 = argc >= 5 && std::strcmp(argv[4], "fp8") == 0;
+    return run_reduce(argv[2], argc >= 4 ? std::atoi(argv[3]) : 3, fp8);
   }
   if (argc >= 3 && std::strcmp(argv[1], "copy") == 0) {
     return run_copy(std::strtoull(argv[2], nullptr, 10), argc >= 4 ? std::atoi(argv[3]) : 3);
   }
-  std::fprintf(stderr, "usage: %s routing FILE [STEPS] | copy BYTES [STEPS]\n", argv[0]);
+  std::fprintf(stderr,
+               "usage: %s routing FILE [STEPS] [16bit|weighted|fp8|w4a8|mx] | reduce FILE [STEPS] "
+               "[bf16|fp8] | copy BYTES [STEPS]\n",
+               argv[0]);
   return 1;
 }

@@ -32,6 +32,8 @@ def lib():
         i64, i32 = ctypes.c_int64, ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
+        L.oracle_set_num_threads.restype = i32
         L.oracle_to_f32.argtypes = [i32, vp, f32p, i64]
         L.oracle_from_f32.argtypes = [i32, f32p, vp, i64]
         L.oracle_silu_mul.argtypes = [f32p, f32p, f32p, i64]
@@ -66,6 +68,11 @@ def lib():
 def num_threads():
     """oracle_num_threads: OpenMP threads the oracle's loops use."""
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n):
+    """oracle_set_num_threads: OpenMP threads of later oracle calls."""
+    assert lib().oracle_set_num_threads(int(n)) == 0
 
 
 def _ptr(a):

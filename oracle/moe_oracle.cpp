@@ -272,6 +272,15 @@ extern "C" {
 // Threads the OpenMP loops below use (reported with the CPU baseline).
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+// Sets the OpenMP thread count of later calls (the CPU baseline's 1-thread
+// timings); changes no arithmetic: every loop over tokens computes each
+// token's values in the same order at any thread count.
+int oracle_set_num_threads(int n) {
+  if (n < 1) return -1;
+  omp_set_num_threads(n);
+  return 0;
+}
+
 // ------------------------------------------------------------ conversions --
 // Element-wise storage conversions, exported so the tests can pin them
 // against library conversions and hand-made tie cases.

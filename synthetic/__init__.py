@@ -172,18 +172,19 @@ def make_moe_inputs(cfg, device="cpu", T=None, seed=None, weights=True):
     return out
 
 
-def make_reduce_inputs(T, K, H, dtype="bf16", seed=4, mask_frac=0.1, device="cpu", R=None):
+def make_reduce_inputs(T, K, H, dtype="bf16", seed=4, mask_frac=0.1, device="cpu", R=None,
+                       rows=True):
     """Inputs of a standalone weighted reduce.
 
-    expert_out [R, H] ~ N(0, 1) (R = T*K by default); topk_weights [T, K]
-    ~ U(0, 1) normalised per row over all K slots; token_topk_to_pos = a
-    seeded random permutation of [0, T*K) (taken mod R when R < T*K) with
-    floor(mask_frac * T * K) seeded slots set to -1.
+    expert_out [R, H] ~ N(0, 1) (R = T*K by default; None when rows=False);
+    topk_weights [T, K] ~ U(0, 1) normalised per row over all K slots;
+    token_topk_to_pos = a seeded random permutation of [0, T*K) (taken mod R
+    when R < T*K) with floor(mask_frac * T * K) seeded slots set to -1.
     """
     dt = DTYPES[dtype]
     P = T * K
     R = P if R is None else R
-    x = normal((R, H), 1.0, seed, S_RED_X, dt, device)
+    x = normal((R, H), 1.0, seed, S_RED_X, dt, device) if rows else None
     w = uniform_tensor((T, K), seed, S_RED_W, device)
     w = (w / w.sum(dim=-1, keepdim=True)).contiguous()
     perm_keys = bits64(seed, S_RED_PERM, 0, P, device)
