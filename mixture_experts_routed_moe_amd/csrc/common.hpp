@@ -94,6 +94,31 @@ __device__ __forceinline__ void static_for(F&& f) {
 // SiLU(g) = g / (1 + e^-g), in fp32.
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// v_mfma_f32_32x32x16_{bf16,f16}: c += A (32 x 16) * B (16 x 32). Lane l
+// supplies A row l % 32 and B column l % 32, reduction elements
+// 8 * (l / 32) .. + 7 of the 16; the result lane l holds column l % 32 and,
+// in register i, row 8 * (i / 4) + 4 * (l / 32) + i % 4.
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's vector loads but the newest N
+// are complete, and so are its LDS accesses.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14], expcnt [6:4] (7 = no
+  // wait), lgkmcnt [11:8] (0 = wait for all).
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 // A workgroup barrier that waits for no memory counter (the caller issues
 // the s_waitcnt it needs first) but is a compiler-level memory fence: no LDS
 // or global access is moved across it.

@@ -98,17 +98,6 @@ struct GemmArgs {
   int n, kd, block_m, n_tiles;
 };
 
-template <int DT>
-__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (DT == kBF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-}
-
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -442,17 +431,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
 // prefetch exists, and the last S..2S-1 chunks run as a guarded tail.
 constexpr int kAGroupElems = 8 * kChunkK;   // one 8-row group of a stage: 1 KB
 
-// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's vector loads but the newest N
-// are complete, and so are its LDS accesses (the A tile it staged must be
-// written before the barrier that publishes it).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
-  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14], expcnt [6:4] (7 = no
-  // wait), lgkmcnt [11:8] (0 = wait for all).
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-}
-
 // Wait until at most `after` chunks of `ops` loads each are outstanding
 // (s_waitcnt takes an immediate: one case per possible count).
 template <int OPS, int MAXAFTER>
@@ -612,33 +590,19 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& g, uint16_t* lds_ring,
   }
 }
 
+// One (row block, column tile) of the wide design: the block's rows
+// m_start .. m_start + rows - 1 of expert e, column tile nt. lds_ring: the
+// double-buffered A stage (2 * NAMAX * 4 * kAGroupElems elements); wrow:
+// the block's row weights staged in LDS (down with routing weights; visible
+// after the pass's first barrier), or unused.
 template <int DT, bool GATEUP, int S, int NAMAX, bool W8>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_ring[2 * NAMAX * 4 * kAGroupElems];
-
-  const int total = g.active_count[0] * g.n_tiles;
-  const int per_xcd = (total + 7) >> 3;
-  const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
-  const int ab = natural / g.n_tiles;
-  const int nt = natural - ab * g.n_tiles;
-  const int bx = g.active_blocks[ab];
-
-  const int e = g.block_expert[bx];
-  const int row_in_group = bx * g.block_m - g.group_padded_offsets[e];
-  const int rows = min(g.block_m, g.group_sizes[e] - row_in_group);
-  if (rows <= 0) return;
-  const int m_start = g.group_offsets[e] + row_in_group;
-
+__device__ __forceinline__ void wide_block(const GemmArgs& g, uint16_t* lds_ring, const float* wrow,
+                                           int e, int nt, int m_start, int rows) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  // Down with routing weights: the block's row weights (<= 256 rows),
-  // staged in LDS for the epilogue.
-  __shared__ float wrow_s[GATEUP ? 1 : kThreads];
-  if (!GATEUP && g.row_w != nullptr && tid < rows) wrow_s[tid] = g.row_w[m_start + tid];
   const int64_t kd = g.kd;
   const int nchunks = g.kd / kChunkK;
   // Start of the reduction walk, as in grouped_gemm_kernel but by column
@@ -678,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
       if (active == na) {
         wide_pass<DT, na, GATEUP, S, NAMAX, W8>(g, lds_ring, a_src, bptr, scale, nchunks, rot, wave,
                                                 lane, lr, lh, m_start + r0, rows_pass, col0,
-                                                wrow_s + r0);
+                                                wrow + r0);
       }
     });
   };
@@ -689,6 +653,32 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g)
     barrier_no_wait();   // every wave is done with the LDS tile
     run_pass(128, int_c<4>{});
   }
+}
+
+template <int DT, bool GATEUP, int S, int NAMAX, bool W8>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_wide_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_ring[2 * NAMAX * 4 * kAGroupElems];
+
+  const int total = g.active_count[0] * g.n_tiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
+  const int ab = natural / g.n_tiles;
+  const int nt = natural - ab * g.n_tiles;
+  const int bx = g.active_blocks[ab];
+
+  const int e = g.block_expert[bx];
+  const int row_in_group = bx * g.block_m - g.group_padded_offsets[e];
+  const int rows = min(g.block_m, g.group_sizes[e] - row_in_group);
+  if (rows <= 0) return;
+  const int m_start = g.group_offsets[e] + row_in_group;
+  // Down with routing weights: the block's row weights (<= 256 rows),
+  // staged in LDS for the epilogue.
+  __shared__ float wrow_s[GATEUP ? 1 : kThreads];
+  if (!GATEUP && g.row_w != nullptr && static_cast<int>(threadIdx.x) < rows) {
+    wrow_s[threadIdx.x] = g.row_w[m_start + threadIdx.x];
+  }
+  wide_block<DT, GATEUP, S, NAMAX, W8>(g, lds_ring, wrow_s, e, nt, m_start, rows);
 }
 
 template <int DT, bool GATEUP, int NAMAX, bool W8>

@@ -30,6 +30,10 @@ struct GemmProblem {
 };
 
 hipError_t launch_gate_up(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+// 16-bit weights, blocks of 128 or 256 rows: one kernel that streams blocks
+// of <= 192 rows through registers and larger ones through an LDS tile.
+hipError_t launch_gate_up_tile(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_down_tile(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 // FP8 E4M3 weights (b0 / b1 hold codes; s0 / s1 the per-row scales).
 hipError_t launch_gate_up_w8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
