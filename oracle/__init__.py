@@ -59,6 +59,8 @@ def lib():
         L.oracle_mx_decode.argtypes = [vp, vp, i64, i32, i32, f32p]
         L.oracle_moe_forward_mx.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, i32p, f32p, i32, i32,
                                             i32, i32, i32, i32p, i32, f32p, f32p, f32p]
+        L.oracle_moe_forward_w8a8.argtypes = [i32, vp, vp, vp, vp, f32p, f32p, f32p, i32p, f32p,
+                                              i32, i32, i32, i32, i32, i32p, i32, f32p, f32p, f32p]
         L.oracle_moe_forward_w4a8.argtypes = [i32, vp, vp, vp, vp, f32p, f32p, f32p, i32p, f32p,
                                               i32, i32, i32, i32, i32, i32p, i32, f32p, f32p, f32p]
         _lib = L
@@ -326,6 +328,29 @@ def moe_forward_w4a8(dt, x, wg4, wu4, wd4, sg, su, sd, ids, w, tokens=None, want
     rc = lib().oracle_moe_forward_w4a8(dt, _ptr(xs), *[_ptr(a) for a in args], _ptr(ids), _ptr(w),
                                        T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
     assert rc == 0, "oracle_moe_forward_w4a8 rejected its arguments"
+    return (y, hp, ep) if want_pairs else y
+
+
+def moe_forward_w8a8(dt, x, wg8, wu8, wd8, sg, su, sd, ids, w, tokens=None, want_pairs=False):
+    """oracle_moe_forward_w8a8: FP8 E4M3 expert weights (codes [E, D, H] /
+    [E, D, H] / [E, H, D], fp32 row scales [E, D] / [E, D] / [E, H]) against
+    FP8 E4M3 activations (x per token, h per routed pair, scale amax / 448).
+    Same outputs as moe_forward."""
+    xs = _storage(x, dt)
+    T, H = xs.shape
+    E, D, _ = wg8.shape
+    K = ids.shape[1]
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tokens is None else len(tok)
+    y = np.empty((n, H), np.float32)
+    hp = np.empty((n * K, D), np.float32) if want_pairs else None
+    ep = np.empty((n * K, H), np.float32) if want_pairs else None
+    args = [_c(a, np.uint8) for a in (wg8, wu8, wd8)] + [_c(a, np.float32) for a in (sg, su, sd)]
+    rc = lib().oracle_moe_forward_w8a8(dt, _ptr(xs), *[_ptr(a) for a in args], _ptr(ids), _ptr(w),
+                                       T, H, D, E, K, _ptr(tok), n, _ptr(y), _ptr(hp), _ptr(ep))
+    assert rc == 0, "oracle_moe_forward_w8a8 rejected its arguments"
     return (y, hp, ep) if want_pairs else y
 
 

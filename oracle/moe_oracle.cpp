@@ -638,6 +638,92 @@ int oracle_moe_forward_w4a8(int dt, const void* x, const uint8_t* wg4, const uin
   return 0;
 }
 
+// ------------------------------------------------------------- W8A8 -------
+// FP8 weights against FP8 activations (the tutorial's module docstring: the
+// weight + activation mode quantises both GEMM operands; the scheme is left
+// open by the pages and taken here as the FP8 weights above with the same
+// per-row E4M3 quantisation applied to the activations):
+//   xq, sx: the E4M3 codes and scale of x[t] (oracle_quantize_fp8_rows of the
+//           row: sx = amax / 448, codes = E4M3(x / sx))
+//   g_j  = dequant_f(sum_h dec(xq[h]) * dec(Wg8[e,j,h]), sx, sg[e,j]),  u_j likewise
+//          (the sum an fp32 fma chain over h ascending; each product of two
+//          E4M3 values is exact in fp32)
+//   h_j  = R(SiLU(g_j) * u_j)                        (dtype dt, as the 16-bit path)
+//   hq, sh: the E4M3 codes and scale of the pair's h row (as xq, sx)
+//   eo_c = R(dequant_f(sum_j dec(hq[j]) * dec(Wd8[e,c,j]), sh, sd[e,c]))
+// with dequant_f(acc, sa, sw) = acc * sa * sw left to right in fp32; y as in
+// oracle_moe_forward. Weights: E4M3 codes [E, D, H] / [E, D, H] / [E, H, D]
+// with fp32 row scales [E*D] / [E*D] / [E*H] (oracle_quantize_fp8_rows).
+int oracle_moe_forward_w8a8(int dt, const void* x, const uint8_t* wg8, const uint8_t* wu8,
+                            const uint8_t* wd8, const float* sg, const float* su, const float* sd,
+                            const int32_t* ids, const float* w, int T, int H, int D, int E, int K,
+                            const int32_t* tokens, int n_tokens, float* y, float* h_pairs,
+                            float* eo_pairs) {
+  if (!dtype_ok(dt) || T < 0 || H <= 0 || D <= 0 || E <= 0 || K <= 0) return -1;
+  if (!sg || !su || !sd) return -1;
+  if (!tokens && n_tokens != T) return -1;
+  for (int i = 0; i < n_tokens; ++i) {
+    const int t = tokens ? tokens[i] : i;
+    if (t < 0 || t >= T) return -1;
+    for (int k = 0; k < K; ++k) {
+      if (ids[static_cast<int64_t>(t) * K + k] >= E) return -1;
+    }
+  }
+  // E4M3 codes and scale of one row of fp32 values (the per-row quantizer).
+  auto quantize_row = [](const float* v, int n, float* codes_as_float) {
+    float amax = 0.0f;
+    for (int k = 0; k < n; ++k) amax = std::fmax(amax, std::fabs(v[k]));
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    for (int k = 0; k < n; ++k) codes_as_float[k] = fp8e4m3_bits_to_float(float_to_fp8e4m3_bits(v[k] / s));
+    return s;
+  };
+#pragma omp parallel
+  {
+    std::vector<float> xrow(H), xq(H), hbuf(D), hq(D), eo(H), acc(H);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < n_tokens; ++i) {
+      const int t = tokens ? tokens[i] : i;
+      for (int c = 0; c < H; ++c) xrow[c] = load_elem(dt, x, static_cast<int64_t>(t) * H + c);
+      const float sx = quantize_row(xrow.data(), H, xq.data());
+      for (int c = 0; c < H; ++c) acc[c] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int64_t slot = static_cast<int64_t>(t) * K + k;
+        const int64_t out_slot = static_cast<int64_t>(i) * K + k;
+        const int e = ids[slot];
+        if (e < 0) {
+          if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = 0.0f;
+          if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = 0.0f;
+          continue;
+        }
+        for (int j = 0; j < D; ++j) {
+          const int64_t row = static_cast<int64_t>(e) * D + j;
+          float ag = 0.0f, au = 0.0f;
+          for (int c = 0; c < H; ++c) {
+            ag = std::fma(xq[c], fp8e4m3_bits_to_float(wg8[row * H + c]), ag);
+            au = std::fma(xq[c], fp8e4m3_bits_to_float(wu8[row * H + c]), au);
+          }
+          const float g = ag * sx * sg[row];
+          const float u = au * sx * su[row];
+          hbuf[j] = round_to(dt, silu(g) * u);
+        }
+        const float sh = quantize_row(hbuf.data(), D, hq.data());
+        for (int c = 0; c < H; ++c) {
+          const int64_t row = static_cast<int64_t>(e) * H + c;
+          float ad = 0.0f;
+          for (int j = 0; j < D; ++j) ad = std::fma(hq[j], fp8e4m3_bits_to_float(wd8[row * D + j]), ad);
+          eo[c] = round_to(dt, ad * sh * sd[row]);
+        }
+        const float wk = w[slot];
+        for (int c = 0; c < H; ++c) acc[c] = std::fma(wk, eo[c], acc[c]);
+        if (h_pairs) for (int j = 0; j < D; ++j) h_pairs[out_slot * D + j] = hbuf[j];
+        if (eo_pairs) for (int c = 0; c < H; ++c) eo_pairs[out_slot * H + c] = eo[c];
+      }
+      for (int c = 0; c < H; ++c) y[static_cast<int64_t>(i) * H + c] = acc[c];
+    }
+  }
+  return 0;
+}
+
 // --------------------------------------------------- MX (block-scaled) ---
 // Block-scaled formats ([B] module docstring: the block-scaled mode, MXFP4 /
 // MXFP8 through gemm_blockscaled with scale factors SFA / SFB; the formats
