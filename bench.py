@@ -534,33 +534,36 @@ def host_info():
             "cpu_model": model, "sockets": len(sockets) or None}
 
 
-def oracle_forward_seconds(cfg, n_tokens, threads=None):
+def oracle_forward_seconds(cfg, n_tokens, dev, threads=None):
     """Seconds the oracle takes for the dispatch of the whole batch plus the
-    forward of its first n_tokens tokens (inputs generated on the host
-    first; generation is not timed), and the token count used."""
+    forward of its first n_tokens tokens, and the token count used. The
+    seeded inputs are generated on the device (the same values as on the
+    host) and the experts those tokens use are copied to the host first;
+    neither is timed."""
     import numpy as np
     import torch
 
     import oracle
     import synthetic as S
-    d = S.make_moe_inputs(cfg, device="cpu")
+    d = S.make_moe_inputs(cfg, device=dev)
     T, K, E = cfg["T"], cfg["K"], cfg["E"]
     n = min(n_tokens, T)
-    ids = d["topk_ids"].numpy()
-    w = d["topk_weights"].numpy()
+    ids = d["topk_ids"].cpu().numpy()
+    w = d["topk_weights"].cpu().numpy()
     sub = ids[:n]
     used = np.unique(sub[sub >= 0])
     remap = np.full(E, -1, np.int32)
     remap[used] = np.arange(used.size, dtype=np.int32)
     sub_ids = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
-    sel = torch.from_numpy(used).long()
+    sel = torch.from_numpy(used).long().to(dev)
     if cfg["dtype"] == "f32":
-        st, dt = (lambda t: t.contiguous().numpy()), oracle.F32
+        st, dt = (lambda t: t.contiguous().cpu().numpy()), oracle.F32
     else:
-        st = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+        st = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
         dt = oracle.BF16 if cfg["dtype"] == "bf16" else oracle.F16
     args = (st(d["x"][:n]), st(d["w_gate"][sel]), st(d["w_up"][sel]), st(d["w_down"][sel]))
     del d
+    torch.cuda.empty_cache()
     prev = oracle.num_threads()
     if threads:
         oracle.set_num_threads(threads)
@@ -574,7 +577,7 @@ def oracle_forward_seconds(cfg, n_tokens, threads=None):
     return sec, n
 
 
-def cpu_baseline(args):
+def cpu_baseline(args, dev):
     """The oracle (as it stands) on bounded samples: the decode workload's
     first --cpu-tokens tokens (the reported value, scaled to the layer), the
     tiny workload whole and the mid-size one on 64 tokens at all threads and
@@ -587,11 +590,11 @@ def cpu_baseline(args):
     for ci, n_tok, one in ((2, args.cpu_tokens, False), (0, 64, True), (1, 64, True),
                            (3, 24, False), (4, 24, False)):
         cfg = S.CONFIGS[ci]
-        sec, n = oracle_forward_seconds(cfg, n_tok)
+        sec, n = oracle_forward_seconds(cfg, n_tok, dev)
         ms = sec * 1e3 * cfg["T"] / n
         e = {"ms_layer": round(ms, 1), "tokens": n}
         if one:
-            sec1, _ = oracle_forward_seconds(cfg, n_tok, threads=1)
+            sec1, _ = oracle_forward_seconds(cfg, n_tok, dev, threads=1)
             e["ms_layer_1thread"] = round(sec1 * 1e3 * cfg["T"] / n, 1)
         per[cfg["name"]] = e
         if ci == 2:
@@ -734,7 +737,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args)
+        cpu = cpu_baseline(args, dev)
         print("# cpu baseline: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
 
     gu = main_s["kernels"]["gate_up"]
