@@ -230,6 +230,24 @@ moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_u
                               int dtype, void* workspace, size_t workspace_bytes, void* y,
                               void* stream);
 
+/* Steps 2-3 without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): moe_routed_forward with its workspace (h, then
+ * expert_out, the layout above) taken from a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (80 MiB: enough for T*K = 4096 routed pairs at
+ * d_hidden 7168, d_expert 2048 in a 16-bit dtype). The caller still passes
+ * every input and y. Same result, requirements and errors as
+ * moe_routed_forward, plus MOE_ERR_WORKSPACE when
+ * moe_forward_workspace_bytes(T, K, H, D, dtype) exceeds the array (nothing
+ * is launched then). No call of it allocates memory. Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents: calls
+ * that overlap on one GPU (on two streams or from two threads) race. */
+#define MOE_NOALLOC_SCRATCH_BYTES (80u << 20)
+moe_status moe_routed_forward_noalloc(const void* x, const void* w_gate, const void* w_up,
+                                      const void* w_down, const moe_tables* tables, int H, int D,
+                                      int dtype, void* y, void* stream);
+
 /* Steps 2-3 with the weighted down epilogue ([B] moe_routed_kernel):
  *   y [T, H] dtype = moe_reduce_fused(moe_expert_down_weighted(
  *                        moe_expert_gate_up(x)), token_topk_to_pos, NULL),

@@ -269,6 +269,25 @@ def moe_routed_forward(x, w_gate, w_up, w_down, tables, y=None, workspace=None,
     return y
 
 
+NOALLOC_SCRATCH_BYTES = 80 << 20   # MOE_NOALLOC_SCRATCH_BYTES of the C header
+
+
+def moe_routed_forward_noalloc(x, w_gate, w_up, w_down, tables, y):
+    """Steps 2-3 with the library's static per-GPU scratch as the workspace
+    (moe_routed_forward_noalloc: no device allocation anywhere in the call;
+    y must be given). Calls that overlap on one GPU race on the scratch."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_tensor(w, n, x.dtype, 3, tables.device)
+    H, D = _expert_shapes(x, w_gate, w_up, w_down, tables, True)
+    _check_tensor(y, "y", x.dtype, 2, tables.device)
+    _require(tuple(y.shape) == (tables.T, H), MOE_ERR_SHAPE, "y must be [T, H]")
+    check(lib().moe_routed_forward_noalloc(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                           tables.ref, H, D, _DTYPE_CODE[x.dtype], _ptr(y),
+                                           _stream(x.device)))
+    return y
+
+
 def moe_routed_forward_weighted(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
     """Steps 2-3 with the weighted down epilogue and an unweighted combine."""
     return moe_routed_forward(x, w_gate, w_up, w_down, tables, y, workspace, True)

@@ -35,6 +35,24 @@ moe_status ok() {
   return MOE_OK;
 }
 
+}  // namespace
+
+namespace moe {
+
+moe_status set_error(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+}  // namespace moe
+
+namespace {
+
 bool block_m_ok(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 bool is_16bit(int dt) { return dt == MOE_F16 || dt == MOE_BF16; }

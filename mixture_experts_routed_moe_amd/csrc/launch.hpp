@@ -10,6 +10,9 @@
 
 namespace moe {
 
+// Sets the calling thread's last-error message (printf-style) and returns s.
+moe_status set_error(moe_status s, const char* fmt, ...);
+
 hipError_t launch_dispatch(const int32_t* topk_ids, const float* topk_weights,
                            const moe_tables& t, hipStream_t stream);
 
