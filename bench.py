@@ -270,11 +270,11 @@ def time_workload(cfg, steps, warmup, block_m, dev, flush, trials, weights="16bi
             mr.moe_expert_down_mx(hq, sh, wd, tables, x.dtype, expert_out=eo)
             ev[5].record()
         elif weights == "w8a8":
-            mr.quantize_fp8_rows(x, q=xq, scales=sx)
+            mr.quantize_fp8_act_rows(x, q=xq, scales=sx)
             ev[2].record()
             mr.moe_expert_gate_up_w8a8(xq, sx, wg, wu, tables, x.dtype, h=h)
             ev[3].record()
-            mr.quantize_fp8_rows(h, q=hq, scales=sh)
+            mr.quantize_fp8_act_rows(h, q=hq, scales=sh)
             ev[4].record()
             mr.moe_expert_down_w8a8(hq, sh, wd, tables, x.dtype, expert_out=eo)
             ev[5].record()

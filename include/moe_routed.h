@@ -358,6 +358,38 @@ moe_status moe_routed_forward_w4a8(const void* x, const uint8_t* w_gate, const u
                                    int dtype, void* workspace, size_t workspace_bytes, void* y,
                                    void* stream);
 
+/* W8A8 experts ([B] module docstring: the weight + activation mode, both
+ * GEMM operands quantised; the scheme is left open by the pages and taken
+ * here as E4M3 codes with one fp32 scale per row on both sides): the FP8
+ * weights of moe_quantize_fp8_rows (codes [E, D, H] / [E, D, H] / [E, H, D],
+ * scales [E, D] / [E, D] / [E, H]) against FP8 activations quantised by the
+ * same call: xq [T, H] with sx [T] (token order; gathered through
+ * sorted_token) and hq [P, D] with sh [P] (sorted order), both 16-byte
+ * aligned. Each dot product is accumulated in fp32 over the exact products
+ * of the E4M3 values (by the FP8 MFMA, in its own order), then scaled once:
+ *   g = (xq[t] . Wg8[e,j]) * sx[t] * s_gate[e,j]  (fp32, left to right),
+ *   u likewise,  h[i, j] = R(SiLU(g) * u),
+ *   expert_out[i, c] = R((hq[i] . Wd8[e,c]) * sh[i] * s_down[e,c]).
+ * dtype (of h / expert_out): MOE_F16 or MOE_BF16; the 16-bit calls' shape
+ * rules. moe_routed_forward_w8a8 runs: x -> xq, sx (moe_quantize_fp8_rows
+ * per token); gate/up -> h; h -> hq, sh (per sorted row); down ->
+ * expert_out; moe_reduce_fused -> y. Its workspace
+ * (moe_forward_w8a8_workspace_bytes, 256-byte aligned): h, expert_out as
+ * moe_routed_forward's, then xq, sx, hq, sh. Errors as the 16-bit calls. */
+moe_status moe_expert_gate_up_w8a8(const uint8_t* xq, const float* sx, const uint8_t* w_gate,
+                                   const uint8_t* w_up, const float* s_gate, const float* s_up,
+                                   const moe_tables* tables, int H, int D, int dtype, void* h,
+                                   void* stream);
+moe_status moe_expert_down_w8a8(const uint8_t* hq, const float* sh, const uint8_t* w_down,
+                                const float* s_down, const moe_tables* tables, int H, int D,
+                                int dtype, void* expert_out, void* stream);
+size_t moe_forward_w8a8_workspace_bytes(int T, int K, int H, int D, int dtype);
+moe_status moe_routed_forward_w8a8(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                   const uint8_t* w_down, const float* s_gate, const float* s_up,
+                                   const float* s_down, const moe_tables* tables, int H, int D,
+                                   int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                   void* stream);
+
 /* Block-scaled (MX) experts ([B] module docstring: the block-scaled mode,
  * gemm_blockscaled with per-block scale factors of both operands; formats
  * as the OCP Microscaling specification v1.0 defines them): along a row,

@@ -387,6 +387,118 @@ def moe_routed_forward_w8(x, w_gate, w_up, w_down, tables, y=None, workspace=Non
     return y
 
 
+def quantize_fp8_act_rows(a, q=None, scales=None):
+    """moe_quantize_fp8_rows on activations a [rows, cols] (fp16 / bf16 /
+    fp32): E4M3 codes (uint8) and fp32 scales amax / 448 per row. Returns
+    (q, scales) (written into q / scales when given)."""
+    _check_tensor(a, "a", None, 2)
+    _require(a.dtype in _DTYPE_CODE, MOE_ERR_DTYPE, "a must be float16, bfloat16 or float32")
+    rows, cols = a.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=a.device)
+    _check_tensor(q, "q", torch.uint8, 2, a.device)
+    _check_tensor(scales, "scales", torch.float32, 1, a.device)
+    _require(tuple(q.shape) == (rows, cols) and scales.numel() == rows, MOE_ERR_SHAPE,
+             "q must be [rows, cols] and scales [rows]")
+    check(lib().moe_quantize_fp8_rows(_ptr(a), rows, cols, _DTYPE_CODE[a.dtype], _ptr(q),
+                                      _ptr(scales), _stream(a.device)))
+    return q, scales
+
+
+def _check_w8a8_act(q, s, name, rows, cols, device):
+    _check_tensor(q, name, torch.uint8, 2, device)
+    _check_tensor(s, name + " scales", torch.float32, 1, device)
+    _require(tuple(q.shape) == (rows, cols) and s.numel() == rows, MOE_ERR_SHAPE,
+             "%s must be [%d, %d] with %d scales" % (name, rows, cols, rows))
+
+
+def moe_expert_gate_up_w8a8(xq, sx, w_gate, w_up, tables, dtype=torch.bfloat16, h=None):
+    """Step 2a with W8A8 experts: E4M3 activations xq [T, H] with per-token
+    scales sx [T] against FP8Weights [E, D, H]; h [P, D] of dtype."""
+    for n, w in (("w_gate", w_gate), ("w_up", w_up)):
+        _check_w8(w, n, tables.device)
+    E, D, H = w_gate.shape
+    _check_w8a8_act(xq, sx, "xq", tables.T, H, tables.device)
+    _require(tuple(w_up.shape) == (E, D, H) and E == tables.E, MOE_ERR_SHAPE,
+             "w_gate and w_up must be [E, D, H]")
+    _require(dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE, "dtype must be 16-bit")
+    if h is None:
+        h = torch.empty(tables.T * tables.K, D, dtype=dtype, device=xq.device)
+    _check_tensor(h, "h", dtype, 2, tables.device)
+    check(lib().moe_expert_gate_up_w8a8(_ptr(xq), _ptr(sx), _ptr(w_gate.codes), _ptr(w_up.codes),
+                                        _ptr(w_gate.scales), _ptr(w_up.scales), tables.ref, H, D,
+                                        _DTYPE_CODE[dtype], _ptr(h), _stream(xq.device)))
+    return h
+
+
+def moe_expert_down_w8a8(hq, sh, w_down, tables, dtype=torch.bfloat16, expert_out=None):
+    """Step 2b with W8A8 experts: E4M3 rows hq [P, D] with per-row scales
+    sh [P] against FP8Weights [E, H, D]; expert_out [P, H] of dtype."""
+    _check_w8(w_down, "w_down", tables.device)
+    E, H, D = w_down.shape
+    _require(E == tables.E, MOE_ERR_SHAPE, "w_down must be [E, H, D]")
+    _check_w8a8_act(hq, sh, "hq", tables.T * tables.K, D, tables.device)
+    _require(dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE, "dtype must be 16-bit")
+    if expert_out is None:
+        expert_out = torch.empty(tables.T * tables.K, H, dtype=dtype, device=hq.device)
+    _check_tensor(expert_out, "expert_out", dtype, 2, tables.device)
+    check(lib().moe_expert_down_w8a8(_ptr(hq), _ptr(sh), _ptr(w_down.codes), _ptr(w_down.scales),
+                                     tables.ref, H, D, _DTYPE_CODE[dtype], _ptr(expert_out),
+                                     _stream(hq.device)))
+    return expert_out
+
+
+def forward_w8a8_workspace(tables, H, D, dtype):
+    """A workspace for moe_routed_forward_w8a8 and views of its buffers:
+    (ws, h, expert_out, xq, sx, hq, sh)."""
+    code = _DTYPE_CODE[dtype]
+    nbytes = lib().moe_forward_w8a8_workspace_bytes(tables.T, tables.K, H, D, code)
+    _require(nbytes > 0, MOE_ERR_SHAPE, "invalid workspace sizes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=tables.device)
+    base = lib().moe_forward_workspace_bytes(tables.T, tables.K, H, D, code)
+    off = lib().moe_forward_workspace_expert_out_offset(tables.T, tables.K, H, D, code)
+    T, P = tables.T, tables.T * tables.K
+    esz = torch.empty((), dtype=dtype).element_size()
+    up = lambda v: (v + 255) // 256 * 256
+    h = ws[:P * D * esz].view(dtype).view(P, D)
+    eo = ws[off:off + P * H * esz].view(dtype).view(P, H)
+    o_xq = base
+    o_sx = o_xq + up(T * H)
+    o_hq = o_sx + up(T * 4)
+    o_sh = o_hq + up(P * D)
+    xq = ws[o_xq:o_xq + T * H].view(T, H)
+    sx = ws[o_sx:o_sx + T * 4].view(torch.float32)
+    hq = ws[o_hq:o_hq + P * D].view(P, D)
+    sh = ws[o_sh:o_sh + P * 4].view(torch.float32)
+    return ws, h, eo, xq, sx, hq, sh
+
+
+def moe_routed_forward_w8a8(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
+    """Steps 2-3 with W8A8 experts (FP8Weights; x 16-bit, quantised to E4M3
+    per token inside, h per sorted row): y [T, H] of x.dtype."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    _require(x.dtype in (torch.float16, torch.bfloat16), MOE_ERR_DTYPE,
+             "W8A8 experts take float16 or bfloat16 activations")
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_w8(w, n, tables.device)
+    H, D = _expert_shapes(x, w_gate, w_up, w_down, tables, True)
+    if workspace is None:
+        workspace = forward_w8a8_workspace(tables, H, D, x.dtype)[0]
+    _check_tensor(workspace, "workspace", torch.uint8, 1, tables.device)
+    if y is None:
+        y = torch.empty(tables.T, H, dtype=x.dtype, device=x.device)
+    _check_tensor(y, "y", x.dtype, 2, tables.device)
+    _require(tuple(y.shape) == (tables.T, H), MOE_ERR_SHAPE, "y must be [T, H]")
+    check(lib().moe_routed_forward_w8a8(_ptr(x), _ptr(w_gate.codes), _ptr(w_up.codes),
+                                        _ptr(w_down.codes), _ptr(w_gate.scales),
+                                        _ptr(w_up.scales), _ptr(w_down.scales), tables.ref, H, D,
+                                        _DTYPE_CODE[x.dtype], _ptr(workspace), workspace.numel(),
+                                        _ptr(y), _stream(x.device)))
+    return y
+
+
 class W4Weights:
     """Stacked expert weights in int4: `packed` uint8 [E, N, Kd/2] (field 2i
     in the low nibble of byte i) and one fp32 scale per row, `scales` [E, N]

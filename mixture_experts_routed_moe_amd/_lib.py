@@ -104,6 +104,15 @@ def lib():
         L.moe_expert_gate_up_w4a8.restype = i32
         L.moe_expert_down_w4a8.argtypes = [vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
         L.moe_expert_down_w4a8.restype = i32
+        L.moe_expert_gate_up_w8a8.argtypes = [vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_gate_up_w8a8.restype = i32
+        L.moe_expert_down_w8a8.argtypes = [vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_down_w8a8.restype = i32
+        L.moe_forward_w8a8_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_forward_w8a8_workspace_bytes.restype = sz
+        L.moe_routed_forward_w8a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp,
+                                              sz, vp, vp]
+        L.moe_routed_forward_w8a8.restype = i32
         L.moe_forward_w4a8_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.moe_forward_w4a8_workspace_bytes.restype = sz
         L.moe_routed_forward_w4a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, tp, i32, i32, i32, vp,

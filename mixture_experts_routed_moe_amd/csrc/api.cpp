@@ -579,6 +579,96 @@ moe_status moe_routed_forward_w4a8(const void* x, const uint8_t* w_gate, const u
   return hip_status(err, "moe_routed_forward_w4a8 reduce launch");
 }
 
+moe_status check_w8a8_shapes(const moe_tables* t, int H, int D, int dtype) {
+  moe_status s = check_expert_shapes(t, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (!is_16bit(dtype)) return fail(MOE_ERR_DTYPE, "W8A8 experts take MOE_F16 or MOE_BF16 outputs");
+  return MOE_OK;
+}
+
+moe_status moe_expert_gate_up_w8a8(const uint8_t* xq, const float* sx, const uint8_t* w_gate,
+                                   const uint8_t* w_up, const float* s_gate, const float* s_up,
+                                   const moe_tables* tables, int H, int D, int dtype, void* h,
+                                   void* stream) {
+  if (!xq || !sx || !w_gate || !w_up || !s_gate || !s_up || !h) {
+    return fail(MOE_ERR_NULL, "xq, sx, w_gate, w_up, s_gate, s_up and h must not be NULL");
+  }
+  moe_status s = check_w8a8_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (reinterpret_cast<uintptr_t>(xq) % 16 != 0) return fail(MOE_ERR_SHAPE, "xq must be 16-byte aligned");
+  moe::GemmProblem p{xq, w_gate, w_up, h, D, H, dtype, s_gate, s_up};
+  p.sa = sx;
+  return hip_status(moe::launch_gate_up_w8a8(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_gate_up_w8a8 launch");
+}
+
+moe_status moe_expert_down_w8a8(const uint8_t* hq, const float* sh, const uint8_t* w_down,
+                                const float* s_down, const moe_tables* tables, int H, int D,
+                                int dtype, void* expert_out, void* stream) {
+  if (!hq || !sh || !w_down || !s_down || !expert_out) {
+    return fail(MOE_ERR_NULL, "hq, sh, w_down, s_down and expert_out must not be NULL");
+  }
+  moe_status s = check_w8a8_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (reinterpret_cast<uintptr_t>(hq) % 16 != 0) return fail(MOE_ERR_SHAPE, "hq must be 16-byte aligned");
+  moe::GemmProblem p{hq, w_down, nullptr, expert_out, H, D, dtype, s_down, nullptr};
+  p.sa = sh;
+  return hip_status(moe::launch_down_w8a8(p, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_down_w8a8 launch");
+}
+
+size_t moe_forward_w8a8_workspace_bytes(int T, int K, int H, int D, int dtype) {
+  const size_t base = moe_forward_workspace_bytes(T, K, H, D, dtype);
+  if (base == 0) return 0;
+  return w4_layout(T, K, H, D, base).total;   // one-byte codes + fp32 row scales
+}
+
+moe_status moe_routed_forward_w8a8(const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                   const uint8_t* w_down, const float* s_gate, const float* s_up,
+                                   const float* s_down, const moe_tables* tables, int H, int D,
+                                   int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                   void* stream) {
+  if (!x || !w_gate || !w_up || !w_down || !s_gate || !s_up || !s_down || !workspace || !y) {
+    return fail(MOE_ERR_NULL,
+                "x, the weights, their scales, workspace and y must not be NULL");
+  }
+  moe_status s = check_w8a8_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  const size_t need = moe_forward_w8a8_workspace_bytes(tables->T, tables->K, H, D, dtype);
+  if (workspace_bytes < need) {
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) {
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const int T = tables->T, K = tables->K;
+  const int64_t P = static_cast<int64_t>(T) * K;
+  char* ws = static_cast<char*>(workspace);
+  const W4Layout L = w4_layout(T, K, H, D, moe_forward_workspace_bytes(T, K, H, D, dtype));
+  void* hbuf = ws;
+  void* eo = ws + moe_forward_workspace_expert_out_offset(T, K, H, D, dtype);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+  float* sx = reinterpret_cast<float*>(ws + L.sx);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+  float* sh = reinterpret_cast<float*>(ws + L.sh);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = moe::launch_quantize_fp8_rows(x, T, H, dtype, xq, sx, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w8a8 x quantisation launch");
+  moe::GemmProblem up{xq, w_gate, w_up, hbuf, D, H, dtype, s_gate, s_up};
+  up.sa = sx;
+  err = moe::launch_gate_up_w8a8(up, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w8a8 gate/up launch");
+  err = moe::launch_quantize_fp8_rows(hbuf, P, D, dtype, hq, sh, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w8a8 h quantisation launch");
+  moe::GemmProblem down{hq, w_down, nullptr, eo, H, D, dtype, s_down, nullptr};
+  down.sa = sh;
+  err = moe::launch_down_w8a8(down, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_w8a8 down launch");
+  err = moe::launch_reduce(eo, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
+                           nullptr, T, K, H, dtype, dtype, y, st);
+  return hip_status(err, "moe_routed_forward_w8a8 reduce launch");
+}
+
 moe_status moe_quantize_mx_rows(const void* v, int64_t rows, int cols, int dtype, int fmt,
                                 uint8_t* codes, uint8_t* scales, void* stream) {
   if (!v || !codes || !scales) return fail(MOE_ERR_NULL, "v, codes and scales must not be NULL");

@@ -11,7 +11,8 @@
 //       moe_dispatch + the forward run STEPS times; per-step times from HIP
 //       events are printed. FORMAT selects the forward: 16bit (default,
 //       moe_routed_forward), weighted (moe_routed_forward_weighted), fp8
-//       (FP8 weights, moe_routed_forward_w8), w4a8 (moe_routed_forward_w4a8)
+//       (FP8 weights, moe_routed_forward_w8), w8a8 (FP8 weights and
+//       activations, moe_routed_forward_w8a8), w4a8 (moe_routed_forward_w4a8)
 //       or mx (moe_routed_forward_mx); the weights are quantised once with
 //       the library's quantizers before the steps.
 //   moe_bench_driver reduce FILE [STEPS] [bf16|fp8]
@@ -135,7 +136,7 @@ int run_copy(size_t bytes, int steps) {
   return 0;
 }
 
-enum Format { kFmt16 = 0, kFmtWeighted, kFmtFp8, kFmtW4a8, kFmtMx };
+enum Format { kFmt16 = 0, kFmtWeighted, kFmtFp8, kFmtW4a8, kFmtMx, kFmtW8a8 };
 
 int parse_format(const char* s) {
   if (!s || std::strcmp(s, "16bit") == 0) return kFmt16;
@@ -143,6 +144,7 @@ int parse_format(const char* s) {
   if (std::strcmp(s, "fp8") == 0) return kFmtFp8;
   if (std::strcmp(s, "w4a8") == 0) return kFmtW4a8;
   if (std::strcmp(s, "mx") == 0) return kFmtMx;
+  if (std::strcmp(s, "w8a8") == 0) return kFmtW8a8;
   return -1;
 }
 
@@ -206,10 +208,10 @@ int run_routing(const char* path, int steps, int fmt) {
   const int64_t rows[3] = {static_cast<int64_t>(E) * D, static_cast<int64_t>(E) * D,
                            static_cast<int64_t>(E) * H};
   const int cols[3] = {H, H, D};
-  if (fmt == kFmtFp8 || fmt == kFmtW4a8 || fmt == kFmtMx) {
+  if (fmt == kFmtFp8 || fmt == kFmtW8a8 || fmt == kFmtW4a8 || fmt == kFmtMx) {
     for (int i = 0; i < 3; ++i) {
       const size_t n = static_cast<size_t>(rows[i]) * cols[i];
-      if (fmt == kFmtFp8) {
+      if (fmt == kFmtFp8 || fmt == kFmtW8a8) {
         q[i] = dmalloc(n);
         s[i] = dmalloc(rows[i] * sizeof(float));
         CHECK_MOE(moe_quantize_fp8_rows(wt[i], rows[i], cols[i], dtype, static_cast<uint8_t*>(q[i]),
@@ -242,6 +244,7 @@ int run_routing(const char* path, int steps, int fmt) {
   size_t wsb = moe_forward_workspace_bytes(T, K, H, D, dtype);
   if (fmt == kFmtW4a8) wsb = moe_forward_w4a8_workspace_bytes(T, K, H, D, dtype);
   if (fmt == kFmtMx) wsb = moe_forward_mx_workspace_bytes(T, K, H, D, dtype);
+  if (fmt == kFmtW8a8) wsb = moe_forward_w8a8_workspace_bytes(T, K, H, D, dtype);
   void* ws = dmalloc(wsb);
   CHECK_HIP(hipDeviceSynchronize());
 
@@ -265,6 +268,11 @@ int run_routing(const char* path, int steps, int fmt) {
         CHECK_MOE(moe_routed_forward_w8(x, qb[0], qb[1], qb[2], static_cast<float*>(s[0]),
                                         static_cast<float*>(s[1]), static_cast<float*>(s[2]),
                                         &tables, H, D, dtype, ws, wsb, y, nullptr));
+        break;
+      case kFmtW8a8:
+        CHECK_MOE(moe_routed_forward_w8a8(x, qb[0], qb[1], qb[2], static_cast<float*>(s[0]),
+                                          static_cast<float*>(s[1]), static_cast<float*>(s[2]),
+                                          &tables, H, D, dtype, ws, wsb, y, nullptr));
         break;
       case kFmtW4a8:
         CHECK_MOE(moe_routed_forward_w4a8(x, qb[0], qb[1], qb[2], static_cast<float*>(s[0]),
@@ -389,7 +397,7 @@ int main(int argc, char** argv) {
     return run_copy(std::strtoull(argv[2], nullptr, 10), argc >= 4 ? std::atoi(argv[3]) : 3);
   }
   std::fprintf(stderr,
-               "usage: %s routing FILE [STEPS] [16bit|weighted|fp8|w4a8|mx] | reduce FILE [STEPS] "
+               "usage: %s routing FILE [STEPS] [16bit|weighted|fp8|w8a8|w4a8|mx] | reduce FILE [STEPS] "
                "[bf16|fp8] | copy BYTES [STEPS]\n",
                argv[0]);
   return 1;

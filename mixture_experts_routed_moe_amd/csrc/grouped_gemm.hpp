@@ -87,6 +87,7 @@ struct GemmArgs {
   const float* s0;     // W8: fp32 scale per row of b0 / b1 (one per output channel)
   const float* s1;
   const float* row_w;  // down: routing weight per output row, or nullptr
+  const float* sa;     // W8A8: fp32 scale per activation row (x: by token; h: by row)
   uint16_t* c;
   const int32_t* sorted_token;
   const int32_t* group_sizes;
@@ -720,6 +721,7 @@ hipError_t launch_typed(const GemmProblem& p, const moe_tables& t, hipStream_t s
   g.s0 = p.s0;
   g.s1 = p.s1;
   g.row_w = GATEUP ? nullptr : p.row_w;
+  g.sa = nullptr;
   g.c = static_cast<uint16_t*>(p.c);
   g.sorted_token = t.sorted_token;
   g.group_sizes = t.group_sizes;

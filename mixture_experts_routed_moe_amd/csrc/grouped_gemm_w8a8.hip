@@ -1,0 +1,93 @@
+// Grouped expert GEMMs with FP8 E4M3 activations against FP8 E4M3 weights
+// (W8A8: the weight + activation mode of the TileLang tutorial ch.18
+// skeletons.py module docstring, both GEMM operands quantised; the scheme,
+// E4M3 with one fp32 scale per row of each operand, is this library's
+// reading of an open choice):
+//   gate/up: g = (xq_t . Wg8[e, j]) * s_x[t] * s_g[e, j],  u likewise,
+//            h[i, j] = R(SiLU(g) * u),  t = sorted_token[i];
+//   down:    eo[i, c] = R((hq_i . Wd8[e, c]) * s_h[i] * s_d[e, c]),
+// each dot product accumulated in fp32 over the exact products of the E4M3
+// codes by the FP8 MFMA, R = rounding to the 16-bit output dtype.
+//
+// Every row block runs the LDS-tiled pass of grouped_gemm_tile.hpp with
+// one-byte operands: 64 reduction elements per chunk (64 bytes per row, the
+// 16-bit tile's layout), one v_mfma_scale_f32_32x32x64_f8f6f4 per fragment
+// pair, twice the MFMA throughput of the 16-bit path per byte of weights
+// (the prefill layer and the hot experts of skewed routing are
+// compute-bound at 16 bits). Scheduling as in grouped_gemm_tile.hip: active
+// row blocks only, expert-local tile-major order dealt out XCD by XCD.
+
+#include "grouped_gemm_tile.hpp"
+
+namespace moe {
+namespace {
+
+template <int DT, bool GATEUP>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_w8a8_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kNBuf * kBufBytes];
+
+  const int total = g.active_count[0] * g.n_tiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
+  const int ab0 = natural / g.n_tiles;
+  const int bx0 = g.active_blocks[ab0];
+  const int e = g.block_expert[bx0];
+  const int first_bx = g.group_padded_offsets[e] / g.block_m;
+  const int first_ab = ab0 - (bx0 - first_bx);
+  const int nblk = (g.group_sizes[e] + g.block_m - 1) / g.block_m;
+  const int local = natural - first_ab * g.n_tiles;
+  const int nt = local / nblk;
+  const int bx = first_bx + (local - nt * nblk);
+
+  const int row_in_group = bx * g.block_m - g.group_padded_offsets[e];
+  const int rows = min(g.block_m, g.group_sizes[e] - row_in_group);
+  if (rows <= 0) return;
+  const int m_start = g.group_offsets[e] + row_in_group;
+  const int nchunks = g.kd / kRowB;      // one-byte elements: 64 per chunk
+  const int rot = nt % nchunks;
+  tile_pass<DT, GATEUP, kRing, true>(g, lds, e, nt, m_start, rows, nchunks, rot, nullptr);
+}
+
+template <int DT, bool GATEUP>
+hipError_t launch_w8a8_typed(const GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  GemmArgs g;
+  g.a = static_cast<const uint16_t*>(p.a);   // FP8 codes, addressed in bytes by the pass
+  g.b0 = p.b0;
+  g.b1 = p.b1;
+  g.s0 = p.s0;
+  g.s1 = p.s1;
+  g.row_w = nullptr;
+  g.sa = p.sa;
+  g.c = static_cast<uint16_t*>(p.c);
+  g.sorted_token = t.sorted_token;
+  g.group_sizes = t.group_sizes;
+  g.group_offsets = t.group_offsets;
+  g.group_padded_offsets = t.group_padded_offsets;
+  g.block_expert = t.block_expert;
+  g.active_blocks = t.active_blocks;
+  g.active_count = t.active_count;
+  g.n = p.n;
+  g.kd = p.kd;
+  g.block_m = t.block_m;
+  g.n_tiles = p.n / (GATEUP ? 128 : 256);
+  const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
+  const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
+  hipLaunchKernelGGL((grouped_gemm_w8a8_kernel<DT, GATEUP>), dim3(grid), dim3(kThreads), 0, stream,
+                     g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_w8a8(const GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  if (p.dtype == kBF16) return launch_w8a8_typed<kBF16, true>(p, t, stream);
+  return launch_w8a8_typed<kF16, true>(p, t, stream);
+}
+
+hipError_t launch_down_w8a8(const GemmProblem& p, const moe_tables& t, hipStream_t stream) {
+  if (p.dtype == kBF16) return launch_w8a8_typed<kBF16, false>(p, t, stream);
+  return launch_w8a8_typed<kF16, false>(p, t, stream);
+}
+
+}  // namespace moe

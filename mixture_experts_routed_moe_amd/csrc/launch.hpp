@@ -30,6 +30,9 @@ struct GemmProblem {
   // sorted_weight), multiplied into each dot product before the rounding to
   // dtype; nullptr = unweighted rows.
   const float* row_w = nullptr;
+  // W8A8 (FP8 activations a with FP8 weights): fp32 scale per activation
+  // row -- x by token (gate/up), h by sorted row (down).
+  const float* sa = nullptr;
 };
 
 hipError_t launch_gate_up(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
@@ -37,6 +40,10 @@ hipError_t launch_gate_up(const GemmProblem& p, const moe_tables& t, hipStream_t
 // of <= 192 rows through registers and larger ones through an LDS tile.
 hipError_t launch_gate_up_tile(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down_tile(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+// W8A8: FP8 E4M3 activations (a, scales sa) against FP8 E4M3 weights (b0 /
+// b1, scales s0 / s1); output c in dtype (kF16 / kBF16).
+hipError_t launch_gate_up_w8a8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+hipError_t launch_down_w8a8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 // FP8 E4M3 weights (b0 / b1 hold codes; s0 / s1 the per-row scales).
 hipError_t launch_gate_up_w8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
