@@ -54,7 +54,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2,
-                    help="index into synthetic.CONFIGS for the main line (default 2: decode T=512)")
+                    help="index into synthetic.CONFIGS for the main line (default 2: decode T=512); "
+                         "with --dump-routing, -1 is the MFMA probe's routing")
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="device bytes written before every timed step (0 = no flush)")
@@ -451,6 +452,10 @@ def time_reduce(args, dev, flush):
     return res
 
 
+PROBE_CFG = dict(name="mfma-probe", dtype="bf16", T=4096, H=7168, D=2048, E=1, K=1,
+                 renorm=False, zipf=False, seed=7)
+
+
 def mfma_probe(args, dev, flush):
     """Labelled MFMA probe (not a workload of the metric): the gate/up and
     down kernels on one expert receiving 4096 rows (T=4096, top-1, E=1,
@@ -460,8 +465,7 @@ def mfma_probe(args, dev, flush):
 
     import mixture_experts_routed_moe_amd as mr
     import synthetic as S
-    cfg = dict(name="mfma-probe", dtype="bf16", T=4096, H=7168, D=2048, E=1, K=1,
-               renorm=False, zipf=False, seed=7)
+    cfg = PROBE_CFG
     d = S.make_moe_inputs(cfg, device=dev)
     tables = mr.moe_dispatch(d["topk_ids"], d["topk_weights"], 1, block_m=256)
     ws, h, eo = mr.forward_workspace(tables, cfg["H"], cfg["D"], torch.bfloat16)
@@ -665,7 +669,9 @@ def main():
         sys.exit(2)
     import synthetic as S
     if args.dump_routing:
-        dump_routing(S.CONFIGS[args.workload], args.block_m, args.dump_routing)
+        cfg = PROBE_CFG if args.workload == -1 else S.CONFIGS[args.workload]
+        dump_routing(cfg, args.block_m or (256 if args.workload == -1 else None),
+                     args.dump_routing)
         return
     if args.dump_reduce:
         dump_reduce(args.dump_reduce)
