@@ -19,9 +19,10 @@ variants in compact form; the full per-kernel detail goes to stderr.
 
 Timing protocol (after the reduce PR's measurement section): warm-up steps,
 then the K timed steps split into 3 trials; before every step a 512 MB
-device buffer is written, which evicts the 4 MB L2s and the 256 MB
+device buffer is read (summed), which evicts the 4 MB L2s and the 256 MB
 last-level cache, so no step reads its inputs from a cache the previous
-step filled; each step is bracketed by HIP events; the value is the median
+step filled, and leaves no dirty lines for the step's own reads to write
+back (--flush-mode write fills the buffer instead); each step is bracketed by HIP events; the value is the median
 of the 3 trial means of the event span (flush excluded). The CPU oracle is
 timed on bounded samples of the workloads under "cpu_baseline".
 
@@ -58,7 +59,9 @@ def parse_args():
                          "with --dump-routing, -1 is the MFMA probe's routing")
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--flush-mb", type=int, default=512,
-                    help="device bytes written before every timed step (0 = no flush)")
+                    help="MB of device memory passed over before every timed step (0 = no flush)")
+    ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
+                    help="read (sum) or write (fill) the flush buffer")
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--no-t4096", action="store_true",
                     help="skip the T=4096 prefill, skewed and small workloads")
@@ -141,17 +144,27 @@ def workload_numbers(d, tables_sizes, weights="16bit", weighted_down=False):
 
 
 class Flusher:
-    """Writes a `mb`-MB device buffer (a fill kernel on the current stream):
-    more than the 256 MB last-level cache and the L2s, so what a timed call
-    reads next comes from HBM."""
+    """Passes over a `mb`-MB device buffer on the current stream, more than
+    the 256 MB last-level cache and the L2s together, so that what a timed
+    call reads next comes from HBM. mode "read" sums the buffer (the caches
+    are left holding clean lines of it); mode "write" fills it, which leaves
+    up to the L2s' size of dirty lines that the timed call's own reads then
+    write back to HBM."""
 
-    def __init__(self, dev, mb):
+    def __init__(self, dev, mb, mode="read"):
         import torch
-        self.buf = torch.empty(max(mb, 0) << 20, dtype=torch.uint8, device=dev) if mb > 0 else None
+        self.buf = torch.ones(max(mb, 0) << 20, dtype=torch.uint8, device=dev) if mb > 0 else None
+        self.mode = mode
+        self.sum_dtype = torch.int32
         self.v = 0
+        self.sink = None
 
     def __call__(self):
-        if self.buf is not None:
+        if self.buf is None:
+            return
+        if self.mode == "read":
+            self.sink = self.buf.sum(dtype=self.sum_dtype)
+        else:
             self.v ^= 1
             self.buf.fill_(self.v)
 
@@ -683,7 +696,7 @@ def main():
         return
     legs = set(args.only.split(",")) if args.only else None
     want = lambda leg: legs is None or leg in legs
-    flush = Flusher(dev, args.flush_mb)
+    flush = Flusher(dev, args.flush_mb, args.flush_mode)
 
     cfg = S.CONFIGS[args.workload]
     main_r = time_workload(cfg, args.steps, args.warmup, args.block_m, dev, flush, args.trials)
@@ -768,9 +781,9 @@ def main():
                      "traffic": traffic, "algo_bytes_per_launch": gu["algo_bytes"],
                      "avg_launch_ms": gu["ms"]},
         "cpu_baseline": cpu,
-        "protocol": "%d trials x ~%d steps, median of trial means; %d MB flush before each "
+        "protocol": "%d trials x ~%d steps, median of trial means; %d MB %s flush before each "
                     "step" % (args.trials, max(1, args.steps // max(1, args.trials)),
-                              args.flush_mb),
+                              args.flush_mb, args.flush_mode),
         "TFLOP_s": main_s["TFLOP_s"], "HBM_GB_s": main_s["HBM_GB_s"],
         "hbm_frac": main_s["hbm_frac"], "mfma_frac": main_s["mfma_frac"],
         "roofline_frac": main_s["roofline_frac"],

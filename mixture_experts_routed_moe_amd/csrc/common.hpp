@@ -65,6 +65,31 @@ __device__ __forceinline__ uint32_t float_to_fp8e4m3(float f) {
   return sign | (static_cast<uint32_t>(e + 7) << 3) | keep;
 }
 
+// Four floats to the E4M3 codes float_to_fp8e4m3 gives, packed a, b, c, d
+// from the low byte up, with gfx950's packed conversion (v_cvt_pk_fp8_f32:
+// OCP E4M3, round to nearest even): magnitudes are clamped to 448 first
+// (med3, so that the conversion never sees an out-of-range value and
+// infinities saturate), and a NaN input takes its code (sign | 0x7f) by a
+// select afterwards.
+__device__ __forceinline__ uint32_t pk4_fp8e4m3(float a, float b, float c, float d) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  const float cc = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  const float cd = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  int q = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+  q = __builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, q, true);
+  uint32_t u = static_cast<uint32_t>(q);
+  const float v[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (v[i] != v[i]) {
+      const uint32_t code = ((__float_as_uint(v[i]) >> 24) & 0x80u) | 0x7fu;
+      u = (u & ~(0xffu << (8 * i))) | (code << (8 * i));
+    }
+  }
+  return u;
+}
+
 template <int DT>
 __device__ __forceinline__ float to_float(uint32_t bits16) {
   if constexpr (DT == kBF16) return bf16_to_float(bits16);

@@ -105,8 +105,7 @@ __device__ __forceinline__ void store_row(void* base, int64_t elem, const float*
     uint32_t q[V / 4];
 #pragma unroll
     for (int i = 0; i < V; i += 4) {
-      q[i / 4] = float_to_fp8e4m3(acc[i]) | (float_to_fp8e4m3(acc[i + 1]) << 8) |
-                 (float_to_fp8e4m3(acc[i + 2]) << 16) | (float_to_fp8e4m3(acc[i + 3]) << 24);
+      q[i / 4] = pk4_fp8e4m3(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
     }
     if constexpr (V % 16 == 0) {
 #pragma unroll

@@ -227,3 +227,31 @@ def test_reduce_fp8_decodes_every_code():
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_reduce_fp8_encodes_every_code_and_tie():
+    # K = 1, unit weight, fp32 in, FP8 out: y is the E4M3 encoding of the
+    # input row itself. Inputs: the value of every finite code, the midpoint
+    # of every pair of neighbouring codes (a tie, which goes to the even
+    # code), one fp32 ulp either side of each midpoint, magnitudes at and
+    # past 448 and infinities (saturate to +-448), values below half the
+    # smallest subnormal (to zero), NaN; both signs (NaN positive only: the
+    # fp32 multiply-add in front of the store does not keep a NaN's sign).
+    # Compared bit for bit with the oracle's encoder.
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.to_f32(codes, oracle.FP8)
+    fin = np.unique(vals[~np.isnan(vals) & (vals >= 0)]).astype(np.float32)
+    mids = ((fin[:-1].astype(np.float64) + fin[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64) * 2, fin[:-1].astype(np.float64) + fin[1:])
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    extra = np.array([448, 449, 463.9, 464, 465, 480, 1e6, 3e38, np.inf,
+                      2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -10, 2.0 ** -20], np.float32)
+    pos_vals = np.concatenate([fin, mids, up, dn, extra])
+    allv = np.concatenate([pos_vals, -pos_vals, np.array([np.nan], np.float32)])
+    H = 256
+    allv = np.concatenate([allv, np.zeros((-len(allv)) % H, np.float32)])
+    x = torch.from_numpy(allv.reshape(-1, H).copy()).to(DEV)
+    R = x.shape[0]
+    pos = torch.arange(R, device=DEV, dtype=torch.int32).view(R, 1)
+    _check_scaled(x, pos, None, None, None, torch.float8_e4m3fn)
