@@ -346,9 +346,11 @@ __global__ __launch_bounds__(256) void quantize_mx_rows_kernel(const void* __res
       for (int i = 0; i < kBlk; ++i) w[i >> 3] |= float_to_fp4e2m1(x[i] / X) << (4 * (i & 7));
       *reinterpret_cast<u32x4*>(codes + r * (cols / 2) + b * (kBlk / 2)) = u32x4{w[0], w[1], w[2], w[3]};
     } else {
-      uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      uint32_t w[8];
 #pragma unroll
-      for (int i = 0; i < kBlk; ++i) w[i >> 2] |= float_to_fp8e4m3(x[i] / X) << (8 * (i & 3));
+      for (int i = 0; i < kBlk; i += 4) {
+        w[i >> 2] = pk4_fp8e4m3(x[i] / X, x[i + 1] / X, x[i + 2] / X, x[i + 3] / X);
+      }
       u32x4* dst = reinterpret_cast<u32x4*>(codes + base + b * kBlk);
       dst[0] = u32x4{w[0], w[1], w[2], w[3]};
       dst[1] = u32x4{w[4], w[5], w[6], w[7]};

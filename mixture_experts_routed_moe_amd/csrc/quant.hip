@@ -73,16 +73,13 @@ __global__ __launch_bounds__(256) void quantize_fp8_rows16_kernel(const uint16_t
 #pragma unroll 4
   for (int v = lane; v < nvec; v += 64) {
     const u32x4 w = row[v];
-    uint32_t packed[2];
+    float f[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t c0 = float_to_fp8e4m3(to_float<DT>(w[j] & 0xffffu) / s);
-      const uint32_t c1 = float_to_fp8e4m3(to_float<DT>(w[j] >> 16) / s);
-      const uint32_t pair = c0 | (c1 << 8);
-      if (j & 1) packed[j >> 1] |= pair << 16;
-      else packed[j >> 1] = pair;
+      f[2 * j] = to_float<DT>(w[j] & 0xffffu) / s;
+      f[2 * j + 1] = to_float<DT>(w[j] >> 16) / s;
     }
-    out[v] = u32x2{packed[0], packed[1]};
+    out[v] = u32x2{pk4_fp8e4m3(f[0], f[1], f[2], f[3]), pk4_fp8e4m3(f[4], f[5], f[6], f[7])};
   }
 }
 
