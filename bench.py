@@ -72,7 +72,7 @@ def parse_args():
                     help="tokens of the decode workload the oracle runs for the CPU baseline")
     ap.add_argument("--only", default=None,
                     help="comma-separated subset of the extra legs to run (t4096, skewed, small, "
-                         "reduce, probe, gate, fp8, w4a8, mx, weighted, w4a8_gemm)")
+                         "reduce, probe, gate, fp8, w8a8, w4a8, mx, weighted, fused, w4a8_gemm)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--dump-routing", default=None, metavar="FILE",
@@ -213,13 +213,15 @@ def timed_calls(fn, n_marks, steps, warmup, flush, trials):
 
 
 def time_workload(cfg, steps, warmup, block_m, dev, flush, trials, weights="16bit",
-                  weighted_down=False):
+                  weighted_down=False, fused=False):
     """One workload's step timed kernel by kernel. weights "fp8" / "w4a8" /
     "mx" / "w8a8": the expert weights are quantized once (timed on its own,
     not part of the step) and the step runs that path's GEMMs (W4A8 / MX /
     W8A8 quantise x and h inside the step, each a timed kernel of its own).
     weighted_down (16-bit weights): the routing weight applied in the down
-    GEMM's epilogue, then an unweighted reduce."""
+    GEMM's epilogue, then an unweighted reduce. fused (16-bit weights,
+    block_m <= 32): gate/up and down in the fused expert kernel, h kept on
+    chip."""
     import torch
 
     import mixture_experts_routed_moe_amd as mr
@@ -251,10 +253,14 @@ def time_workload(cfg, steps, warmup, block_m, dev, flush, trials, weights="16bi
         ws, h, eo, xq, sx, hq, sh = mr.forward_mx_workspace(tables, H, D, x.dtype)
     elif weights == "w8a8":
         ws, h, eo, xq, sx, hq, sh = mr.forward_w8a8_workspace(tables, H, D, x.dtype)
+    elif fused:
+        ws, eo = mr.fused_workspace(tables, H, x.dtype)
     else:
         ws, h, eo = mr.forward_workspace(tables, H, D, x.dtype)
     if weights in ("w4a8", "mx", "w8a8"):
         names = ["dispatch", "quant_x", "gate_up", "quant_h", "down", "reduce"]
+    elif fused:
+        names = ["dispatch", "experts", "reduce"]
     else:
         names = ["dispatch", "gate_up", "down", "reduce"]
     y = torch.empty(T, H, dtype=x.dtype, device=dev)
@@ -292,6 +298,9 @@ def time_workload(cfg, steps, warmup, block_m, dev, flush, trials, weights="16bi
             ev[4].record()
             mr.moe_expert_down_w8a8(hq, sh, wd, tables, x.dtype, expert_out=eo)
             ev[5].record()
+        elif fused:
+            mr.moe_expert_fused(x, wg, wu, wd, tables, expert_out=eo)
+            ev[2].record()
         else:
             if weights == "fp8":
                 mr.moe_expert_gate_up_w8(x, wg, wu, tables, h=h)
@@ -312,6 +321,9 @@ def time_workload(cfg, steps, warmup, block_m, dev, flush, trials, weights="16bi
     per = dict(zip(names, t["parts"]))
     sizes = tables.group_sizes.cpu()
     nums = workload_numbers(d, sizes, weights, weighted_down)
+    if fused:   # h is neither written nor read
+        nums["experts_bytes"] = nums["gate_up_bytes"] + nums["down_bytes"] - 2 * nums["n_valid"] * D * x.element_size()
+        nums["flops_experts"] = nums["flops"]
     return dict(d=d, tables=tables, block_m=block_m, ms=t["span"], trial_ms=t["trial_spans"],
                 wall_incl_flush_ms=t["wall_incl_flush"], kernel_ms=per, nums=nums, gen_s=t_gen,
                 quant_ms=quant_ms, weights=weights, name=cfg["name"], dtype=cfg["dtype"])
@@ -337,7 +349,10 @@ def summarize(r):
         kernels[n] = {"ms": round(per[n], 4), "algo_bytes": nums[key],
                       "GB_s": round(gbs(nums[key], per[n]), 1),
                       "hbm_frac": round(gbs(nums[key], per[n]) / HBM_PEAK_GBS, 4)}
-    for n, key in (("gate_up", "flops_gate_up"), ("down", "flops_down")):
+    for n, key in (("gate_up", "flops_gate_up"), ("down", "flops_down"),
+                   ("experts", "flops_experts")):
+        if n not in per:
+            continue
         kernels[n]["TFLOP_s" if r.get("weights") != "w4a8" else "TOP_s"] = \
             round(nums[key] / (per[n] * 1e-3) / 1e12, 2)
         t_roof = max(nums[n + "_bytes"] / (HBM_PEAK_GBS * 1e9), nums[key] / (peak * 1e12)) * 1e3
@@ -363,7 +378,7 @@ def compact(s):
     return {"ms": s["ms_per_layer"], "roof": s["roofline_frac"], "hbm": s["hbm_frac"],
             "mfma": s["mfma_frac"], "TF": s["TFLOP_s"],
             "k_ms": {n: k[n]["ms"] for n in k},
-            "k_roof": {n: k[n]["roofline_frac"] for n in ("gate_up", "down")}}
+            "k_roof": {n: k[n]["roofline_frac"] for n in ("gate_up", "down", "experts") if n in k}}
 
 
 def run_workload(cfg, args, dev, flush, **kw):
@@ -736,13 +751,13 @@ def main():
             torch.cuda.empty_cache()
         for leg, kw in (("fp8", dict(weights="fp8")), ("w8a8", dict(weights="w8a8")),
                         ("w4a8", dict(weights="w4a8")), ("mx", dict(weights="mx")),
-                        ("weighted", dict(weighted_down=True))):
+                        ("weighted", dict(weighted_down=True)), ("fused", dict(fused=True))):
             if not want(leg):
                 continue
             if leg == "w8a8" and not hasattr(__import__("mixture_experts_routed_moe_amd"),
                                              "moe_expert_gate_up_w8a8"):
                 continue
-            for ci in (2, 3):
+            for ci in ((2,) if leg == "fused" else (2, 3)):
                 s = run_workload(S.CONFIGS[ci], args, dev, flush, **kw)
                 extras.setdefault(leg, {})["T%d" % S.CONFIGS[ci]["T"]] = s
                 variants["%s_T%d" % (leg, S.CONFIGS[ci]["T"])] = [s["ms_per_layer"],

@@ -230,6 +230,37 @@ moe_status moe_routed_forward(const void* x, const void* w_gate, const void* w_u
                               int dtype, void* workspace, size_t workspace_bytes, void* y,
                               void* stream);
 
+/* Steps 2a + 2b fused for decode-sized row blocks ([A] "stage-2 down",
+ * which notes that the two stages can be fused so that h is never stored):
+ * one workgroup per row block computes the block's h (at most 32 rows x D)
+ * into on-chip memory (LDS), then the block's expert_out rows from it.
+ *   expert_out [P, H] dtype output, bit-identical to
+ *              moe_expert_down(moe_expert_gate_up(x)) (same rounding of h,
+ *              same summation order).
+ * Requires tables built with block_m <= 32, D <= MOE_FUSED_MAX_D_EXPERT
+ * (h of a block must fit in LDS), dtype MOE_BF16 or MOE_F16, and the
+ * requirements of moe_expert_gate_up.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_UNSUPPORTED
+ * (block_m > 32 or D > MOE_FUSED_MAX_D_EXPERT), MOE_ERR_HIP. */
+#define MOE_FUSED_MAX_D_EXPERT 2048
+moe_status moe_expert_fused(const void* x, const void* w_gate, const void* w_up,
+                            const void* w_down, const moe_tables* tables, int H, int D,
+                            int dtype, void* expert_out, void* stream);
+
+/* Workspace of moe_routed_forward_fused: expert_out [P, H] dtype only (no h).
+ * 0 if the sizes are invalid. */
+size_t moe_fused_workspace_bytes(int T, int K, int H, int dtype);
+
+/* Steps 2-3 with the fused expert kernel: y [T, H] dtype =
+ * moe_reduce_fused(moe_expert_fused(x), token_topk_to_pos, topk_weights),
+ * bit-identical to moe_routed_forward. `workspace` holds expert_out
+ * (moe_fused_workspace_bytes, 256-byte aligned).
+ * Errors: as moe_expert_fused and moe_reduce_fused, plus MOE_ERR_WORKSPACE. */
+moe_status moe_routed_forward_fused(const void* x, const void* w_gate, const void* w_up,
+                                    const void* w_down, const moe_tables* tables, int H, int D,
+                                    int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                    void* stream);
+
 /* Steps 2-3 without allocation, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): moe_routed_forward with its workspace (h, then

@@ -269,6 +269,59 @@ def moe_routed_forward(x, w_gate, w_up, w_down, tables, y=None, workspace=None,
     return y
 
 
+FUSED_MAX_D_EXPERT = 2048   # MOE_FUSED_MAX_D_EXPERT of the C header
+
+
+def moe_expert_fused(x, w_gate, w_up, w_down, tables, expert_out=None):
+    """Steps 2a + 2b in one kernel for tables with block_m <= 32 (h of each
+    row block stays in LDS): expert_out [T*K, H], bit-identical to
+    moe_expert_down(moe_expert_gate_up(x))."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_tensor(w, n, x.dtype, 3, tables.device)
+    H, D = _expert_shapes(x, w_gate, w_up, w_down, tables, True)
+    P = tables.T * tables.K
+    if expert_out is None:
+        expert_out = torch.empty(P, H, dtype=x.dtype, device=x.device)
+    _check_tensor(expert_out, "expert_out", x.dtype, 2, tables.device)
+    _require(tuple(expert_out.shape) == (P, H), MOE_ERR_SHAPE, "expert_out must be [T*K, H]")
+    check(lib().moe_expert_fused(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), tables.ref, H,
+                                 D, _DTYPE_CODE[x.dtype], _ptr(expert_out), _stream(x.device)))
+    return expert_out
+
+
+def fused_workspace(tables, H, dtype):
+    """A workspace for moe_routed_forward_fused (expert_out only) and its
+    expert_out view."""
+    nbytes = lib().moe_fused_workspace_bytes(tables.T, tables.K, H, _DTYPE_CODE[dtype])
+    _require(nbytes > 0, MOE_ERR_SHAPE, "invalid workspace sizes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=tables.device)
+    P = tables.T * tables.K
+    esz = torch.empty((), dtype=dtype).element_size()
+    return ws, ws[:P * H * esz].view(dtype).view(P, H)
+
+
+def moe_routed_forward_fused(x, w_gate, w_up, w_down, tables, y=None, workspace=None):
+    """Steps 2-3 with the fused expert kernel (moe_routed_forward_fused):
+    y [T, H], bit-identical to moe_routed_forward; `workspace` from
+    fused_workspace() (allocated here when None)."""
+    _check_tensor(x, "x", None, 2, tables.device)
+    for n, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_tensor(w, n, x.dtype, 3, tables.device)
+    H, D = _expert_shapes(x, w_gate, w_up, w_down, tables, True)
+    if workspace is None:
+        workspace = fused_workspace(tables, H, x.dtype)[0]
+    _check_tensor(workspace, "workspace", torch.uint8, 1, tables.device)
+    if y is None:
+        y = torch.empty(tables.T, H, dtype=x.dtype, device=x.device)
+    _check_tensor(y, "y", x.dtype, 2, tables.device)
+    _require(tuple(y.shape) == (tables.T, H), MOE_ERR_SHAPE, "y must be [T, H]")
+    check(lib().moe_routed_forward_fused(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                         tables.ref, H, D, _DTYPE_CODE[x.dtype], _ptr(workspace),
+                                         workspace.numel(), _ptr(y), _stream(x.device)))
+    return y
+
+
 NOALLOC_SCRATCH_BYTES = 80 << 20   # MOE_NOALLOC_SCRATCH_BYTES of the C header
 
 

@@ -73,6 +73,12 @@ def lib():
         L.moe_routed_forward.restype = i32
         L.moe_routed_forward_noalloc.argtypes = [vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
         L.moe_routed_forward_noalloc.restype = i32
+        L.moe_expert_fused.argtypes = [vp, vp, vp, vp, tp, i32, i32, i32, vp, vp]
+        L.moe_expert_fused.restype = i32
+        L.moe_fused_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.moe_fused_workspace_bytes.restype = sz
+        L.moe_routed_forward_fused.argtypes = [vp, vp, vp, vp, tp, i32, i32, i32, vp, sz, vp, vp]
+        L.moe_routed_forward_fused.restype = i32
         L.moe_expert_down_weighted.argtypes = [vp, vp, tp, i32, i32, i32, vp, vp]
         L.moe_expert_down_weighted.restype = i32
         L.moe_routed_forward_weighted.argtypes = [vp, vp, vp, vp, tp, i32, i32, i32, vp, sz, vp,

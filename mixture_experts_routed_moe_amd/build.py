@@ -22,7 +22,7 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-Wall"]
 KERNEL_SOURCES = ["gate.hip", "dispatch.hip", "grouped_gemm.hip", "grouped_gemm_tile.hip",
-                  "grouped_gemm_w8.hip", "grouped_gemm_w8a8.hip",
+                  "grouped_gemm_w8.hip", "grouped_gemm_w8a8.hip", "grouped_gemm_fused.hip",
                   "grouped_gemm_f32.hip", "quant.hip", "reduce.hip", "w4a8.hip", "mx.hip",
                   "noalloc.hip"]
 HOST_SOURCES = ["api.cpp"]

@@ -387,6 +387,67 @@ moe_status moe_routed_forward_weighted(const void* x, const void* w_gate, const 
                         workspace_bytes, y, stream, true);
 }
 
+static moe_status check_fused(const moe_tables* tables, int H, int D, int dtype) {
+  moe_status s = check_expert_shapes(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  if (!is_16bit(dtype)) return fail(MOE_ERR_DTYPE, "the fused expert kernel takes MOE_F16 or MOE_BF16");
+  if (tables->block_m > 32) {
+    return fail(MOE_ERR_UNSUPPORTED, "the fused expert kernel needs tables with block_m <= 32 (got %d)",
+                tables->block_m);
+  }
+  if (D > moe::fused_max_d_expert()) {
+    return fail(MOE_ERR_UNSUPPORTED, "the fused expert kernel holds h in LDS: D <= %d (got %d)",
+                moe::fused_max_d_expert(), D);
+  }
+  return MOE_OK;
+}
+
+moe_status moe_expert_fused(const void* x, const void* w_gate, const void* w_up,
+                            const void* w_down, const moe_tables* tables, int H, int D,
+                            int dtype, void* expert_out, void* stream) {
+  if (!x || !w_gate || !w_up || !w_down || !expert_out) {
+    return fail(MOE_ERR_NULL, "x, w_gate, w_up, w_down and expert_out must not be NULL");
+  }
+  moe_status s = check_fused(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  moe::GemmProblem up{x, w_gate, w_up, nullptr, D, H, dtype};
+  moe::GemmProblem down{nullptr, w_down, nullptr, expert_out, H, D, dtype};
+  return hip_status(moe::launch_fused_expert(up, down, *tables, static_cast<hipStream_t>(stream)),
+                    "moe_expert_fused launch");
+}
+
+size_t moe_fused_workspace_bytes(int T, int K, int H, int dtype) {
+  if (T < 1 || K < 1 || H <= 0 || !is_float(dtype)) return 0;
+  return align_up(static_cast<size_t>(T) * K * H * dtype_bytes(dtype));
+}
+
+moe_status moe_routed_forward_fused(const void* x, const void* w_gate, const void* w_up,
+                                    const void* w_down, const moe_tables* tables, int H, int D,
+                                    int dtype, void* workspace, size_t workspace_bytes, void* y,
+                                    void* stream) {
+  if (!x || !w_gate || !w_up || !w_down || !workspace || !y) {
+    return fail(MOE_ERR_NULL, "x, w_gate, w_up, w_down, workspace and y must not be NULL");
+  }
+  moe_status s = check_fused(tables, H, D, dtype);
+  if (s != MOE_OK) return s;
+  const size_t need = moe_fused_workspace_bytes(tables->T, tables->K, H, dtype);
+  if (workspace_bytes < need) {
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) {
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe::GemmProblem up{x, w_gate, w_up, nullptr, D, H, dtype};
+  moe::GemmProblem down{nullptr, w_down, nullptr, workspace, H, D, dtype};
+  hipError_t err = moe::launch_fused_expert(up, down, *tables, st);
+  if (err != hipSuccess) return hip_status(err, "moe_routed_forward_fused expert launch");
+  const int64_t P = static_cast<int64_t>(tables->T) * tables->K;
+  err = moe::launch_reduce(workspace, P, tables->token_topk_to_pos, tables->topk_weights, nullptr,
+                           nullptr, tables->T, tables->K, H, dtype, dtype, y, st);
+  return hip_status(err, "moe_routed_forward_fused reduce launch");
+}
+
 moe_status moe_quantize_fp8_rows(const void* w, int64_t rows, int cols, int dtype, uint8_t* q,
                                  float* scales, void* stream) {
   if (!w || !q || !scales) return fail(MOE_ERR_NULL, "w, q and scales must not be NULL");

@@ -13,8 +13,9 @@
 //       moe_routed_forward), weighted (moe_routed_forward_weighted), fp8
 //       (FP8 weights, moe_routed_forward_w8), w8a8 (FP8 weights and
 //       activations, moe_routed_forward_w8a8), w4a8 (moe_routed_forward_w4a8)
-//       or mx (moe_routed_forward_mx); the weights are quantised once with
-//       the library's quantizers before the steps.
+//       or mx (moe_routed_forward_mx), the weights quantised once with the
+//       library's quantizers before the steps; or fused
+//       (moe_routed_forward_fused: tables with block_m <= 32).
 //   moe_bench_driver reduce FILE [STEPS] [bf16|fp8]
 //       The standalone moe_reduce_fused of a dump written by `bench.py
 //       --dump-reduce FILE`: header {magic, T, K, H} then token_topk_to_pos
@@ -136,7 +137,7 @@ int run_copy(size_t bytes, int steps) {
   return 0;
 }
 
-enum Format { kFmt16 = 0, kFmtWeighted, kFmtFp8, kFmtW4a8, kFmtMx, kFmtW8a8 };
+enum Format { kFmt16 = 0, kFmtWeighted, kFmtFp8, kFmtW4a8, kFmtMx, kFmtW8a8, kFmtFused };
 
 int parse_format(const char* s) {
   if (!s || std::strcmp(s, "16bit") == 0) return kFmt16;
@@ -145,6 +146,7 @@ int parse_format(const char* s) {
   if (std::strcmp(s, "w4a8") == 0) return kFmtW4a8;
   if (std::strcmp(s, "mx") == 0) return kFmtMx;
   if (std::strcmp(s, "w8a8") == 0) return kFmtW8a8;
+  if (std::strcmp(s, "fused") == 0) return kFmtFused;
   return -1;
 }
 
@@ -178,7 +180,7 @@ int run_routing(const char* path, int steps, int fmt) {
     std::fprintf(stderr, "%s is truncated\n", path);
     return 1;
   }
-  if (fmt != kFmt16 && fmt != kFmtWeighted && dtype == MOE_F32) {
+  if (fmt != kFmt16 && fmt != kFmtWeighted && fmt != kFmtFused && dtype == MOE_F32) {
     std::fprintf(stderr, "quantised formats need a 16-bit dtype\n");
     return 1;
   }
@@ -245,6 +247,7 @@ int run_routing(const char* path, int steps, int fmt) {
   if (fmt == kFmtW4a8) wsb = moe_forward_w4a8_workspace_bytes(T, K, H, D, dtype);
   if (fmt == kFmtMx) wsb = moe_forward_mx_workspace_bytes(T, K, H, D, dtype);
   if (fmt == kFmtW8a8) wsb = moe_forward_w8a8_workspace_bytes(T, K, H, D, dtype);
+  if (fmt == kFmtFused) wsb = moe_fused_workspace_bytes(T, K, H, dtype);
   void* ws = dmalloc(wsb);
   CHECK_HIP(hipDeviceSynchronize());
 
@@ -259,6 +262,10 @@ int run_routing(const char* path, int steps, int fmt) {
       case kFmt16:
         CHECK_MOE(moe_routed_forward(x, wt[0], wt[1], wt[2], &tables, H, D, dtype, ws, wsb, y,
                                      nullptr));
+        break;
+      case kFmtFused:
+        CHECK_MOE(moe_routed_forward_fused(x, wt[0], wt[1], wt[2], &tables, H, D, dtype, ws, wsb,
+                                           y, nullptr));
         break;
       case kFmtWeighted:
         CHECK_MOE(moe_routed_forward_weighted(x, wt[0], wt[1], wt[2], &tables, H, D, dtype, ws,
@@ -397,7 +404,7 @@ int main(int argc, char** argv) {
     return run_copy(std::strtoull(argv[2], nullptr, 10), argc >= 4 ? std::atoi(argv[3]) : 3);
   }
   std::fprintf(stderr,
-               "usage: %s routing FILE [STEPS] [16bit|weighted|fp8|w8a8|w4a8|mx] | reduce FILE [STEPS] "
+               "usage: %s routing FILE [STEPS] [16bit|weighted|fp8|w8a8|w4a8|mx|fused] | reduce FILE [STEPS] "
                "[bf16|fp8] | copy BYTES [STEPS]\n",
                argv[0]);
   return 1;

@@ -197,14 +197,17 @@ __device__ __forceinline__ void weight_rows(const GemmArgs& g, int e, int nt, in
 // waits for B fragments of later chunks, so S-1 chunks of weights stay in
 // flight across the per-chunk barrier. The loop body is straight-line (no
 // branch touches the accumulators, so they stay in place); the last chunks
-// run as a guarded tail without prefetches past the end.
-template <int DT, int NA, int RG, bool GATEUP, int S, bool W8, int CK>
+// run as a guarded tail without prefetches past the end. HLDS (gate/up):
+// the rounded h values go to h_lds[row * ldh + column] in LDS instead of
+// g.c (the fused expert kernel keeps a block's h on chip).
+template <int DT, int NA, int RG, bool GATEUP, int S, bool W8, int CK, bool HLDS = false>
 __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[32 * RG][CK + 8],
                                           const uint16_t* const* asrc,
                                           const uint8_t* const* bptr, const float* scale,
                                           int nchunks, int rot, int a_row, int a_seg, int lr,
                                           int lh, int64_t out_row0, int rows_pass, int col0,
-                                          const float* wrow) {
+                                          const float* wrow, uint16_t* h_lds = nullptr,
+                                          int ldh = 0) {
   f32x16 acc[NA][2];
 #pragma unroll
   for (int q = 0; q < NA; ++q) {
@@ -301,7 +304,12 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
           v1 *= scale[1];
         }
         if constexpr (GATEUP) {
-          out[0] = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
+          const uint16_t hv = static_cast<uint16_t>(from_float<DT>(silu(v0) * v1));
+          if constexpr (HLDS) {
+            h_lds[row * ldh + col0 + lr] = hv;
+          } else {
+            out[0] = hv;
+          }
         } else {
           if (weighted) {   // the row's routing weight, before the rounding
             const float w = wrow[row];

@@ -45,6 +45,11 @@ hipError_t launch_down_tile(const GemmProblem& p, const moe_tables& t, hipStream
 hipError_t launch_gate_up_w8a8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down_w8a8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
+// Gate/up and down of each row block in one workgroup (block_m <= 32,
+// d_expert <= fused_max_d_expert()), h kept in LDS; up.c is unused.
+hipError_t launch_fused_expert(const GemmProblem& up, const GemmProblem& down,
+                               const moe_tables& t, hipStream_t stream);
+int fused_max_d_expert();
 // FP8 E4M3 weights (b0 / b1 hold codes; s0 / s1 the per-row scales).
 hipError_t launch_gate_up_w8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
 hipError_t launch_down_w8(const GemmProblem& p, const moe_tables& t, hipStream_t stream);
