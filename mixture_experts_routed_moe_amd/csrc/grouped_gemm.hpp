@@ -53,6 +53,8 @@
 
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -155,6 +157,26 @@ struct BChunk {
 
 
 
+// Eight FP8 E4M3 codes (bytes of w, in order) -> eight 16-bit values of
+// dtype DT, exactly (every E4M3 value is a bf16 and an fp16 value).
+template <int DT>
+__device__ __forceinline__ u32x4 fp8x8_to_16bit(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t d = w[i >> 1];
+    const bool hi = i & 1;
+    if constexpr (DT == kBF16) {
+      r[i] = hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true))
+                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false));
+    } else {
+      r[i] = hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true))
+                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false));
+    }
+  }
+  return r;
+}
+
 // The two weight rows a lane streams and their scales: gate/up -- row col0
 // + lane%32 of W_gate and of W_up (col0 = 128*nt + 32*wave); down -- rows
 // col0 + lane%32 and col0 + 32 + lane%32 of W_down (col0 = 256*nt +
@@ -199,8 +221,14 @@ __device__ __forceinline__ void weight_rows(const GemmArgs& g, int e, int nt, in
 // branch touches the accumulators, so they stay in place); the last chunks
 // run as a guarded tail without prefetches past the end. HLDS (gate/up):
 // the rounded h values go to h_lds[row * ldh + column] in LDS instead of
-// g.c (the fused expert kernel keeps a block's h on chip).
-template <int DT, int NA, int RG, bool GATEUP, int S, bool W8, int CK, bool HLDS = false>
+// g.c (the fused expert kernel keeps a block's h on chip). A8 (with W8):
+// the A rows are FP8 E4M3 codes (asrc holds byte addresses; 8 codes per
+// thread and segment), decoded exactly to DT when staged into LDS, and each
+// dot product is scaled by its activation row's scale g.sa before the
+// weight row's: (sum * s_a) * s_w, the products of two E4M3 values being
+// exact in fp32 as on the FP8 MFMA.
+template <int DT, int NA, int RG, bool GATEUP, int S, bool W8, int CK, bool HLDS = false,
+          bool A8 = false>
 __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[32 * RG][CK + 8],
                                           const uint16_t* const* asrc,
                                           const uint8_t* const* bptr, const float* scale,
@@ -219,7 +247,8 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
   // row group).
   constexpr int kARows = 256 / (CK / 8);
   constexpr int kSub = 32 / kARows;
-  u32x4 aring[S][NA][kSub];
+  using ARaw = std::conditional_t<A8, u32x2, u32x4>;   // one segment as loaded
+  ARaw aring[S][NA][kSub];
   BChunk<DT, W8, CK> bring[S];
 
   auto load_chunk = [&](int c, int slot) __attribute__((always_inline)) {
@@ -231,7 +260,12 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
 #pragma unroll
       for (int sb = 0; sb < kSub; ++sb) {
         if (a_row + kARows * sb + 32 * q < rows_pass) {
-          aring[slot][q][sb] = load16(asrc[q * kSub + sb] + off);
+          if constexpr (A8) {
+            aring[slot][q][sb] = *reinterpret_cast<const u32x2*>(
+                reinterpret_cast<const uint8_t*>(asrc[q * kSub + sb]) + off);
+          } else {
+            aring[slot][q][sb] = load16(asrc[q * kSub + sb] + off);
+          }
         }
       }
     }
@@ -243,7 +277,15 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
 #pragma unroll
       for (int sb = 0; sb < kSub; ++sb) {
         const int r = a_row + kARows * sb + 32 * q;
-        if (r < rows_pass) *reinterpret_cast<u32x4*>(&lds_a[buf][r][a_seg * 8]) = aring[slot][q][sb];
+        if (r < rows_pass) {
+          u32x4 v;
+          if constexpr (A8) {
+            v = fp8x8_to_16bit<DT>(aring[slot][q][sb]);
+          } else {
+            v = aring[slot][q][sb];
+          }
+          *reinterpret_cast<u32x4*>(&lds_a[buf][r][a_seg * 8]) = v;
+        }
       }
     }
   };
@@ -299,7 +341,11 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
       if (row < rows_pass) {
         uint16_t* out = g.c + (out_row0 + row) * g.n + col0 + lr;
         float v0 = acc[q][0][i], v1 = acc[q][1][i];
-        if constexpr (W8) {   // the rows' scales, once per dot product
+        if constexpr (A8) {   // the activation row's scale, then the weight rows'
+          const float sa = g.sa[GATEUP ? g.sorted_token[out_row0 + row] : out_row0 + row];
+          v0 = v0 * sa * scale[0];
+          v1 = v1 * sa * scale[1];
+        } else if constexpr (W8) {   // the rows' scales, once per dot product
           v0 *= scale[0];
           v1 *= scale[1];
         }
@@ -328,7 +374,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& g, uint16_t (*lds_a)[3
 // block); GATEUP selects the gate/up kernel (two weight matrices, gathered A,
 // SiLU(gate)*up epilogue) or the down kernel (one matrix, 64 columns per
 // wave, contiguous A); S = software-pipeline depth in chunks.
-template <int DT, int RG, bool GATEUP, int S, bool W8>
+template <int DT, int RG, bool GATEUP, int S, bool W8, bool A8 = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   // Reduction elements per chunk: 64; 128 with FP8 weights, so a lane still
   // loads 64 contiguous bytes of each weight row per chunk (two lanes cover
@@ -396,18 +442,23 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
         int r = a_row + kARows * sb + 32 * q;
         if (r >= rows_pass) r = 0;
         const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
-        asrc[q * kSub + sb] = g.a + src * kd + a_seg * 8;
+        if constexpr (A8) {   // byte addresses of FP8 codes
+          asrc[q * kSub + sb] = reinterpret_cast<const uint16_t*>(
+              reinterpret_cast<const uint8_t*>(g.a) + src * kd + a_seg * 8);
+        } else {
+          asrc[q * kSub + sb] = g.a + src * kd + a_seg * 8;
+        }
       }
     }
     const int64_t out_row0 = m_start + r0;
     if (active == RG) {
-      gemm_pass<DT, RG, RG, GATEUP, S, W8, CK>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
-                                           a_seg, lr, lh, out_row0, rows_pass, col0,
-                                           wrow_s + r0);
+      gemm_pass<DT, RG, RG, GATEUP, S, W8, CK, false, A8>(g, lds_a, asrc, bptr, scale, nchunks,
+                                                          rot, a_row, a_seg, lr, lh, out_row0,
+                                                          rows_pass, col0, wrow_s + r0);
     } else if constexpr (RG == 2) {
-      gemm_pass<DT, 1, RG, GATEUP, S, W8, CK>(g, lds_a, asrc, bptr, scale, nchunks, rot, a_row,
-                                          a_seg, lr, lh, out_row0, rows_pass, col0,
-                                          wrow_s + r0);
+      gemm_pass<DT, 1, RG, GATEUP, S, W8, CK, false, A8>(g, lds_a, asrc, bptr, scale, nchunks,
+                                                         rot, a_row, a_seg, lr, lh, out_row0,
+                                                         rows_pass, col0, wrow_s + r0);
     }
   }
 }
@@ -704,17 +755,17 @@ void launch_wide(unsigned grid, const GemmArgs& g, hipStream_t stream) {
   }
 }
 
-template <int DT, int RG, bool GATEUP, int S, bool W8>
+template <int DT, int RG, bool GATEUP, int S, bool W8, bool A8 = false>
 void launch_rg(unsigned grid, const GemmArgs& g, hipStream_t stream) {
   // Depth S needs at least S chunks (kd / 64, or kd / 128 with FP8 weights;
   // >= 1 by the shape rules); fall back to depth 2 below that (a single
   // chunk runs the tail alone).
   if (g.kd / (W8 ? 128 : kChunkK) >= S) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<DT, RG, GATEUP, S, W8>), dim3(grid), dim3(kThreads),
-                       0, stream, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<DT, RG, GATEUP, S, W8, A8>), dim3(grid),
+                       dim3(kThreads), 0, stream, g);
   } else {
-    hipLaunchKernelGGL((grouped_gemm_kernel<DT, RG, GATEUP, 2, W8>), dim3(grid), dim3(kThreads),
-                       0, stream, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<DT, RG, GATEUP, 2, W8, A8>), dim3(grid),
+                       dim3(kThreads), 0, stream, g);
   }
 }
 

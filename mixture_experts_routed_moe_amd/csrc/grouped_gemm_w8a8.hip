@@ -9,13 +9,18 @@
 // each dot product accumulated in fp32 over the exact products of the E4M3
 // codes by the FP8 MFMA, R = rounding to the 16-bit output dtype.
 //
-// Every row block runs the LDS-tiled pass of grouped_gemm_tile.hpp with
-// one-byte operands: 64 reduction elements per chunk (64 bytes per row, the
-// 16-bit tile's layout), one v_mfma_scale_f32_32x32x64_f8f6f4 per fragment
-// pair, twice the MFMA throughput of the 16-bit path per byte of weights
-// (the prefill layer and the hot experts of skewed routing are
+// Blocks of 128 or 256 rows run the LDS-tiled pass of grouped_gemm_tile.hpp
+// with one-byte operands: 64 reduction elements per chunk (64 bytes per row,
+// the 16-bit tile's layout), one v_mfma_scale_f32_32x32x64_f8f6f4 per
+// fragment pair, twice the MFMA throughput of the 16-bit path per byte of
+// weights (the prefill layer and the hot experts of skewed routing are
 // compute-bound at 16 bits). Scheduling as in grouped_gemm_tile.hip: active
 // row blocks only, expert-local tile-major order dealt out XCD by XCD.
+// Blocks of at most 64 rows (decode), bound by the weight stream, run the
+// FP8-weight register-streaming kernels of grouped_gemm.hpp in their A8
+// form: the activation codes are decoded exactly to the 16-bit dtype as they
+// are staged, so each product of two E4M3 values is exact in fp32 as on the
+// FP8 MFMA (the sums may differ in order only).
 
 #include "grouped_gemm_tile.hpp"
 
@@ -73,8 +78,20 @@ hipError_t launch_w8a8_typed(const GemmProblem& p, const moe_tables& t, hipStrea
   g.n_tiles = p.n / (GATEUP ? 128 : 256);
   const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
   const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
-  hipLaunchKernelGGL((grouped_gemm_w8a8_kernel<DT, GATEUP>), dim3(grid), dim3(kThreads), 0, stream,
-                     g);
+  if (t.block_m <= 64) {
+    // Decode-sized blocks are bound by the weight stream: the register-
+    // streaming kernels of the FP8-weight path, with the activation codes
+    // decoded exactly to DT in the A staging (the same sums of exact
+    // products, on the 16-bit MFMA) and both row scales in the epilogue.
+    if (t.block_m <= 32) {
+      launch_rg<DT, 1, GATEUP, kStagesRG1W8, true, true>(grid, g, stream);
+    } else {
+      launch_rg<DT, 2, GATEUP, kStagesRG2, true, true>(grid, g, stream);
+    }
+  } else {
+    hipLaunchKernelGGL((grouped_gemm_w8a8_kernel<DT, GATEUP>), dim3(grid), dim3(kThreads), 0,
+                       stream, g);
+  }
   return hipGetLastError();
 }
 
