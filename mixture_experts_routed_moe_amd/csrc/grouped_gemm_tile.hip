@@ -49,8 +49,10 @@
 //   * Scheduling: only row blocks holding rows run. Within an expert the
 //     (block, column tile) pairs are ordered tile-major, so the row blocks of
 //     a hot expert that share a weight tile are adjacent, run together on one
-//     XCD (workgroup L runs on XCD L % 8, and each XCD takes a contiguous
-//     range of the order) and read that tile through its L2 once.
+//     XCD and read that tile through its L2 once; granules of positions are
+//     dealt out to the XCDs in turn and run alternately from both ends of
+//     the expert order (tile_order_position), which spreads a hot expert's
+//     tiles over every XCD and mixes them with small experts' tiles.
 
 #include "grouped_gemm_tile.hpp"
 
@@ -63,9 +65,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_tile_kernel(GemmArgs g)
   __shared__ float wrow_s[GATEUP ? 1 : kTileRows];
 
   const int total = g.active_count[0] * g.n_tiles;
-  const int per_xcd = (total + 7) >> 3;
-  const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
+  const int natural = tile_order_position(blockIdx.x, total, g.n_tiles);
+  if (natural >= total) return;
   // Expert-local tile-major order: the expert of position `natural` in the
   // block-major order owns the same range in both orders.
   const int ab0 = natural / g.n_tiles;
@@ -119,11 +120,12 @@ hipError_t launch_tile_typed(const GemmProblem& p, const moe_tables& t, hipStrea
   g.block_m = t.block_m;
   g.n_tiles = p.n / (GATEUP ? 128 : 256);
   const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
-  const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
   if (g.kd / kChunkK < kStagesWide) {
     // reductions shorter than the register design's pipeline: that design alone
+    const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
     launch_wide<DT, GATEUP, kWideNaMax, false>(grid, g, stream);
   } else {
+    const unsigned grid = static_cast<unsigned>(tile_order_grid(total, g.n_tiles));
     hipLaunchKernelGGL((grouped_gemm_tile_kernel<DT, GATEUP>), dim3(grid), dim3(kThreads), 0,
                        stream, g);
   }

@@ -31,6 +31,37 @@ constexpr int kRing = 3;
 constexpr int kStreamNa = kWideNaMax;
 constexpr int kTileMinRows = 32 * kStreamNa + 1;
 
+// Placement of the (row block, column tile) positions on the XCDs:
+// workgroup L runs on XCD L % 8; the positions are cut into granules of G
+// (the column-tile count, so a one-block expert's column tiles are one
+// granule and share the block's activation rows in one L2), granule i
+// belongs to XCD i % 8, and each XCD runs its granules alternately from the
+// front and the back of the expert order (first, last, second, second-last,
+// ...). In the expert-local tile-major order a hot expert's positions --
+// column tile by column tile, each tile's row blocks together -- are thus
+// dealt out over every XCD (contiguous per-XCD ranges put a 16-block
+// expert's 256 compute-bound tiles on one or two XCDs), and on each XCD its
+// compute-bound granules run beside the memory-bound ones of small experts.
+// Returns `total` for workgroups past the XCD's granules.
+__device__ __forceinline__ int tile_order_position(int L, int total, int G) {
+  const int x = L & 7;
+  const int j = L >> 3;
+  const int k = j / G;
+  const int r = j - k * G;
+  const int ng = (total + G - 1) / G;
+  const int ngx = (ng - x + 7) >> 3;          // granules x, x + 8, ... below ng
+  if (k >= ngx) return total;
+  const int idx = (k & 1) ? ngx - 1 - (k >> 1) : (k >> 1);
+  return (x + 8 * idx) * G + r;
+}
+
+// Workgroups that reach every position of any launch with at most
+// `positions` positions.
+inline int64_t tile_order_grid(int64_t positions, int G) {
+  const int64_t granules = (positions + G - 1) / G;
+  return (granules + 7) / 8 * 8 * G;
+}
+
 // A thread's loads of one chunk: NAL activation rows and 4 weight rows.
 template <int NAL>
 struct Slot {

@@ -15,7 +15,8 @@
 // fragment pair, twice the MFMA throughput of the 16-bit path per byte of
 // weights (the prefill layer and the hot experts of skewed routing are
 // compute-bound at 16 bits). Scheduling as in grouped_gemm_tile.hip: active
-// row blocks only, expert-local tile-major order dealt out XCD by XCD.
+// row blocks only, expert-local tile-major order dealt out to the XCDs in
+// granules.
 // Blocks of at most 64 rows (decode), bound by the weight stream, run the
 // FP8-weight register-streaming kernels of grouped_gemm.hpp in their A8
 // form: the activation codes are decoded exactly to the 16-bit dtype as they
@@ -32,9 +33,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_w8a8_kernel(GemmArgs g)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kNBuf * kBufBytes];
 
   const int total = g.active_count[0] * g.n_tiles;
-  const int per_xcd = (total + 7) >> 3;
-  const int natural = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if ((blockIdx.x >> 3) >= per_xcd || natural >= total) return;
+  const int natural = tile_order_position(blockIdx.x, total, g.n_tiles);
+  if (natural >= total) return;
   const int ab0 = natural / g.n_tiles;
   const int bx0 = g.active_blocks[ab0];
   const int e = g.block_expert[bx0];
@@ -89,7 +89,8 @@ hipError_t launch_w8a8_typed(const GemmProblem& p, const moe_tables& t, hipStrea
       launch_rg<DT, 2, GATEUP, kStagesRG2, true, true>(grid, g, stream);
     }
   } else {
-    hipLaunchKernelGGL((grouped_gemm_w8a8_kernel<DT, GATEUP>), dim3(grid), dim3(kThreads), 0,
+    const unsigned tgrid = static_cast<unsigned>(tile_order_grid(total, g.n_tiles));
+    hipLaunchKernelGGL((grouped_gemm_w8a8_kernel<DT, GATEUP>), dim3(tgrid), dim3(kThreads), 0,
                        stream, g);
   }
   return hipGetLastError();
