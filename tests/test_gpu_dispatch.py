@@ -56,7 +56,8 @@ def _random(T, K, E, mask, seed):
 @pytest.mark.parametrize("BM", BMS)
 @pytest.mark.parametrize("T,K,E,mask", [(1, 1, 1, 0.0), (5, 2, 3, 0.0), (37, 8, 16, 0.2),
                                          (300, 8, 256, 0.05), (2000, 6, 1000, 0.1),
-                                         (129, 8, 1024, 0.0), (40, 4, 5, 1.0)])
+                                         (129, 8, 1024, 0.0), (40, 4, 5, 1.0),
+                                         (128, 8, 64, 0.1), (205, 5, 40, 0.0)])
 def test_dispatch_random(T, K, E, mask, BM):
     ids, w = _random(T, K, E, mask, seed=T * 3 + K + E)
     _compare(ids, w, E, BM)
