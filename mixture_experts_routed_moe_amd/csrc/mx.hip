@@ -72,6 +72,15 @@ struct MxChunk {
   uint32_t sa[NA];
 };
 
+// Scale words of two consecutive chunks, loaded together (PAIR form): for
+// each weight row and activation row the 16 bytes [h0, h1] of chunk c and
+// [h0, h1] of chunk c + 1.
+template <int NA>
+struct MxScalePair {
+  u32x4 sw[2];
+  u32x4 sa[NA];
+};
+
 struct MxGroupedArgs {
   const uint8_t* a;         // gate/up: xq [T, kd] E4M3; down: hq [P, kd]
   const uint8_t* as;        // their E8M0 scales [rows, kd/32]
@@ -95,17 +104,26 @@ struct MxGroupedArgs {
 // of 32 * NAS rows). asrc[2q + sb]: this thread's staging row of group q
 // (row 32q + a_row + 16 sb); ascale[q]: the lane's activation row 32q + lr,
 // at its lane-half's scale bytes; bptr / bscale: the lane's two weight rows.
-template <int NA, int NAS>
+//
+// PAIR (reduction length a multiple of 512 and no rotation of the chunk
+// walk): the scale words are loaded once per two chunks, 16 bytes per row
+// at every even chunk (scale rows are then 16-byte aligned and hold an even
+// number of chunks); the even chunk reads its lane half's word h, the odd
+// chunk the word 2 + h, copied to its ring slot before the next even load
+// overwrites the pair.
+template <int NA, int NAS, bool PAIR = false>
 __device__ __forceinline__ void mx_pass(const uint8_t* const* asrc, const uint8_t* const* ascale,
                                         int a_row, int a_seg, const uint8_t* const* bptr,
                                         const uint8_t* const* bscale, int nch, int rot, int rows_pass,
                                         int lr, int lh, uint8_t (*lds)[32 * NAS][kLdsRow],
                                         f32x16* acc) {
   constexpr int S = kStages;
+  static_assert(!PAIR || S == 2, "paired scale loads assume a 2-deep ring (even chunks in slot 0)");
 #pragma unroll
   for (int q = 0; q < 2 * NA; ++q) acc[q] = f32x16{};
   u32x4 aring[S][2 * NA];
   MxChunk<NA> ring[S];
+  MxScalePair<NA> pair;
 
   auto load_chunk = [&](int ci, int slot) __attribute__((always_inline)) {
     int c = ci + rot;                       // chunks are walked from `rot` on
@@ -117,9 +135,18 @@ __device__ __forceinline__ void mx_pass(const uint8_t* const* asrc, const uint8_
     for (int q = 0; q < 2 * NA; ++q) {
       aring[slot][q] = *reinterpret_cast<const u32x4*>(asrc[q] + static_cast<int64_t>(c) * kCK);
     }
+    if constexpr (PAIR) {
+      if ((c & 1) == 0) {   // this chunk's and the next one's scale words
 #pragma unroll
-    for (int q = 0; q < NA; ++q) {
-      ring[slot].sa[q] = *reinterpret_cast<const uint32_t*>(ascale[q] + c * (kCK / kBlk));
+        for (int q = 0; q < NA; ++q) {
+          pair.sa[q] = *reinterpret_cast<const u32x4*>(ascale[q] - lh * 4 + c * (kCK / kBlk));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        ring[slot].sa[q] = *reinterpret_cast<const uint32_t*>(ascale[q] + c * (kCK / kBlk));
+      }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -127,7 +154,29 @@ __device__ __forceinline__ void mx_pass(const uint8_t* const* asrc, const uint8_
       for (int i = 0; i < 4; ++i) {
         ring[slot].w[j][i] = *reinterpret_cast<const u32x4*>(bptr[j] + static_cast<int64_t>(c) * (kCK / 2) + i * 16);
       }
-      ring[slot].sw[j] = *reinterpret_cast<const uint32_t*>(bscale[j] + c * (kCK / kBlk));
+      if constexpr (PAIR) {
+        if ((c & 1) == 0) {
+          pair.sw[j] = *reinterpret_cast<const u32x4*>(bscale[j] - lh * 4 + c * (kCK / kBlk));
+        }
+      } else {
+        ring[slot].sw[j] = *reinterpret_cast<const uint32_t*>(bscale[j] + c * (kCK / kBlk));
+      }
+    }
+  };
+  // PAIR: the even chunk (slot 0) takes word h of the pair and hands word
+  // 2 + h to the odd chunk's slot.
+  auto take_pair = [&](auto U) __attribute__((always_inline)) {
+    if constexpr (PAIR && decltype(U)::value == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        ring[0].sw[j] = lh ? pair.sw[j].y : pair.sw[j].x;
+        ring[1].sw[j] = lh ? pair.sw[j].w : pair.sw[j].z;
+      }
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        ring[0].sa[q] = lh ? pair.sa[q].y : pair.sa[q].x;
+        ring[1].sa[q] = lh ? pair.sa[q].w : pair.sa[q].z;
+      }
     }
   };
   auto stage_a = [&](int slot, int buf) __attribute__((always_inline)) {
@@ -148,6 +197,7 @@ __device__ __forceinline__ void mx_pass(const uint8_t* const* asrc, const uint8_
   static_assert(S % 2 == 0, "the LDS buffer of chunk i is i % 2 == slot % 2");
   auto step = [&](int c, auto U, bool prefetch, bool stage) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
+    take_pair(U);   // before this step's prefetch of the next pair (S = 2: chunk c + 1 is odd)
     if (prefetch) load_chunk(c + S - 1, (u + S - 1) % S);
     constexpr int buf = u & 1;
     static_for<4>([&](auto TT) {
@@ -187,8 +237,9 @@ __device__ __forceinline__ void mx_pass(const uint8_t* const* asrc, const uint8_
 // W_gate and W_up, writes h = R(SiLU(g) * u); down: columns 256 nt + 64 w +
 // l%32 and + 32 of W_down, writes expert_out), rows in passes of up to
 // 32 * NAMAX.
-template <int DT, bool GATEUP, int NAMAX>
+template <int DT, bool GATEUP, int NAMAX, bool PAIR = false>
 __global__ __launch_bounds__(kThreads) void mx_grouped_kernel(MxGroupedArgs g) {
+  static_assert(!PAIR || NAMAX == 1, "paired scale loads need the unrotated walk of single-group passes");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][32 * NAMAX][kLdsRow];
 
   const int total = g.active_count[0] * g.n_tiles;
@@ -255,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void mx_grouped_kernel(MxGroupedArgs g) {
     f32x16 acc[2 * NAMAX];
     auto run = [&](auto NAC) __attribute__((always_inline)) {
       constexpr int na = decltype(NAC)::value;
-      mx_pass<na, NAMAX>(asrc, ascale, a_row, a_seg, bptr, bscale, nch, rot, rows_pass, lr, lh, lds,
+      mx_pass<na, NAMAX, PAIR>(asrc, ascale, a_row, a_seg, bptr, bscale, nch, rot, rows_pass, lr, lh, lds,
                          acc);
 #pragma unroll
       for (int q = 0; q < na; ++q) {
@@ -398,7 +449,15 @@ hipError_t launch_grouped(const MxGemmProblem& p, const moe_tables& t, hipStream
   g.n_tiles = p.n / (GATEUP ? 128 : 256);
   const int64_t total = static_cast<int64_t>(t.num_blocks) * g.n_tiles;
   const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
-  if (t.block_m <= 32) {
+  // Paired scale loads: 16-byte loads of two chunks' scale words, which
+  // need scale rows of a multiple of 16 bytes (kd a multiple of 512, so an
+  // even chunk count) and 16-byte aligned scale arrays.
+  const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  const bool pair = p.kd % (2 * kCK) == 0 && al16(p.as) && al16(p.s0) && (!GATEUP || al16(p.s1));
+  if (t.block_m <= 32 && pair) {
+    hipLaunchKernelGGL((mx_grouped_kernel<DT, GATEUP, 1, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, g);
+  } else if (t.block_m <= 32) {
     hipLaunchKernelGGL((mx_grouped_kernel<DT, GATEUP, 1>), dim3(grid), dim3(kThreads), 0, stream, g);
   } else if (t.block_m == 64) {
     hipLaunchKernelGGL((mx_grouped_kernel<DT, GATEUP, 2>), dim3(grid), dim3(kThreads), 0, stream, g);

@@ -78,7 +78,16 @@ def _exact_rows(rng, rows, cols, fmt):
     return (v * 2.0 ** np.repeat(k, 32, axis=1)).astype(np.float32)
 
 
-def _down_case(T, H, D, E, K, block_m, seed):
+def _shifted(a, shift):
+    """Device copy of uint8 array a whose data starts `shift` bytes past an
+    aligned allocation (shift 0: a plain copy)."""
+    buf = torch.empty(a.size + shift, dtype=torch.uint8, device=DEV)
+    v = buf[shift:].view(a.shape)
+    v.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+    return v
+
+
+def _down_case(T, H, D, E, K, block_m, seed, scale_shift=0):
     mr = _mr()
     rng = np.random.default_rng(seed)
     ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
@@ -96,9 +105,9 @@ def _down_case(T, H, D, E, K, block_m, seed):
     tables = mr.moe_dispatch(torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), E,
                              block_m=block_m)
     wmx = mr.MXWeights(torch.from_numpy(wc.reshape(E, H, D // 2)).to(DEV),
-                       torch.from_numpy(ws.reshape(E, H, D // 32)).to(DEV))
+                       _shifted(ws.reshape(E, H, D // 32), scale_shift))
     eo = torch.full((P, H), float("nan"), dtype=torch.bfloat16, device=DEV)
-    mr.moe_expert_down_mx(torch.from_numpy(hc).to(DEV), torch.from_numpy(hs).to(DEV), wmx, tables,
+    mr.moe_expert_down_mx(torch.from_numpy(hc).to(DEV), _shifted(hs, scale_shift), wmx, tables,
                           torch.bfloat16, expert_out=eo)
     torch.cuda.synchronize()
     sizes = tables.group_sizes.cpu().numpy()
@@ -118,6 +127,17 @@ def _down_case(T, H, D, E, K, block_m, seed):
 @pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
 def test_down_mx_exact(block_m):
     _down_case(T=200, H=512, D=512, E=5, K=3, block_m=block_m, seed=block_m + 1)
+
+
+# Reduction lengths of an odd (768) and an even (1024) number of 256-long
+# chunks, and scale arrays 4 bytes off a 16-byte boundary: the down GEMM
+# loads two chunks' scale words at once only for an even chunk count and
+# 16-byte aligned scales, and takes the per-chunk loads otherwise.
+@pytest.mark.parametrize("D,block_m,shift", [(768, 16, 0), (1024, 32, 0), (1024, 16, 4),
+                                             (1024, 64, 4)])
+def test_down_mx_exact_scale_loads(D, block_m, shift):
+    _down_case(T=120, H=256, D=D, E=4, K=2, block_m=block_m, seed=D + block_m + shift,
+               scale_shift=shift)
 
 
 def _mx_weights(d):
