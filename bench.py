@@ -57,7 +57,8 @@ def parse_args():
     ap.add_argument("--workload", type=int, default=2,
                     help="index into synthetic.CONFIGS for the main line (default 2: decode T=512); "
                          "with --dump-routing, -1 is the MFMA probe's routing")
-    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--block-m", type=int, default=None,
+                    help="row block size of every timed workload (default: chosen per workload)")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="MB of device memory passed over before every timed step (0 = no flush)")
     ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
@@ -383,7 +384,7 @@ def compact(s):
 
 def run_workload(cfg, args, dev, flush, **kw):
     import torch
-    r = time_workload(cfg, args.steps, args.warmup, None, dev, flush, args.trials, **kw)
+    r = time_workload(cfg, args.steps, args.warmup, args.block_m, dev, flush, args.trials, **kw)
     r.pop("d")
     r.pop("tables")
     torch.cuda.empty_cache()

@@ -95,16 +95,26 @@ __device__ __forceinline__ f32x16 mfma_fp8(u32x4 a_lo, u32x4 a_hi, u32x4 b_lo, u
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// One pass over the reduction for a block of at most 256 rows. R =
-// register-ring depth. FP8: operands of one byte (activations with a scale
-// per row in g.sa, weights with a scale per row in g.s0 / g.s1).
-template <int DT, bool GATEUP, int R, bool FP8 = false>
+// LDS bytes of one buffer of the tile with NQ row groups per wave: 64 NQ
+// activation rows and 256 weight rows of 64 bytes.
+template <int NQ>
+constexpr int tile_buf_bytes() { return (64 * NQ + 256) * kRowB; }
+
+// One pass over the reduction for a block of at most 64 NQ rows (NQ = A
+// fragments per wave per k-slice: the 2 x 2 wave layout gives each wave
+// 32 NQ activation rows; a smaller NQ skips the MFMAs of row groups a block
+// does not have). R = register-ring depth. FP8: operands of one byte
+// (activations with a scale per row in g.sa, weights with a scale per row
+// in g.s0 / g.s1).
+template <int DT, bool GATEUP, int R, bool FP8 = false, int NQ = 4>
 __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e, int nt,
                                           int m_start, int rows, int nchunks, int rot,
                                           const float* wrow) {
+  static_assert(NQ >= 1 && NQ <= 4, "row groups per wave");
   constexpr int EB = FP8 ? 1 : 2;          // bytes per operand element
-  constexpr int NAL = 4;                   // activation rows each thread loads per chunk
-  constexpr int NQ = 4;                    // A fragments per wave per k-slice
+  constexpr int NAL = NQ;                  // activation rows each thread loads per chunk
+  constexpr int ABytes = 64 * NQ * kRowB;  // A part of one LDS buffer
+  constexpr int BufBytes = tile_buf_bytes<NQ>();
   constexpr int NB = 4;                    // B fragments per wave per k-slice
   constexpr int L = NAL + 4;               // loads per thread per chunk
   constexpr int NMF = NQ * NB;             // MFMAs per wave per k-slice
@@ -154,7 +164,7 @@ __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e
   const int fr_off1 = fr * kRowB + 16 * ((2 + (lane >> 5)) ^ f_sw);
   // Fragment rows of this wave (tile rows, A and B).
   const int rh = wave >> 1, ch = wave & 1;
-  const int a_row0 = 128 * rh;
+  const int a_row0 = 32 * NQ * rh;
   int b_rows[NB];
   if constexpr (GATEUP) {
     b_rows[0] = 64 * ch;
@@ -199,22 +209,22 @@ __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e
   auto write_one = [&](auto SLOT, auto BUF, auto I) __attribute__((always_inline)) {
     constexpr int s = decltype(SLOT)::value;
     constexpr int i = decltype(I)::value;
-    uint8_t* w = lds + decltype(BUF)::value * kBufBytes + w_off;
+    uint8_t* w = lds + decltype(BUF)::value * BufBytes + w_off;
     if constexpr (i < NAL) {
       *reinterpret_cast<u32x4*>(w + i * 4096) = ring[s].a[i];
     } else {
-      *reinterpret_cast<u32x4*>(w + kABytes + (i - NAL) * 4096) = ring[s].b[i - NAL];
+      *reinterpret_cast<u32x4*>(w + ABytes + (i - NAL) * 4096) = ring[s].b[i - NAL];
     }
   };
   auto read_frags = [&](auto BUF, auto SL) __attribute__((always_inline)) {
     constexpr int sl = decltype(SL)::value;
-    const uint8_t* base = lds + decltype(BUF)::value * kBufBytes + (sl ? fr_off1 : fr_off0);
+    const uint8_t* base = lds + decltype(BUF)::value * BufBytes + (sl ? fr_off1 : fr_off0);
     // A0 and B0 first: the first MFMA of the slice needs them.
     fa[sl][0] = *reinterpret_cast<const u32x4*>(base + a_row0 * kRowB);
-    fb[sl][0] = *reinterpret_cast<const u32x4*>(base + kABytes + b_rows[0] * kRowB);
+    fb[sl][0] = *reinterpret_cast<const u32x4*>(base + ABytes + b_rows[0] * kRowB);
 #pragma unroll
     for (int j = 1; j < NB; ++j) {
-      fb[sl][j] = *reinterpret_cast<const u32x4*>(base + kABytes + b_rows[j] * kRowB);
+      fb[sl][j] = *reinterpret_cast<const u32x4*>(base + ABytes + b_rows[j] * kRowB);
     }
 #pragma unroll
     for (int q = 1; q < NQ; ++q) {
@@ -284,6 +294,9 @@ __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e
         if constexpr (m < L) write_one(int_c<slot2>{}, int_c<buf2>{}, int_c<m>{});
         __builtin_amdgcn_sched_barrier(0);
       });
+      static_for<(L > NMF ? L - NMF : 0)>([&](auto M) {   // writes beyond the slice's MFMAs
+        write_one(int_c<slot2>{}, int_c<buf2>{}, int_c<NMF + decltype(M)::value>{});
+      });
       read_frags(int_c<buf1>{}, int_c<0>{});
       __builtin_amdgcn_sched_barrier(0);
       static_for<NMF>([&](auto M) {
@@ -291,6 +304,9 @@ __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e
         acc[m / NB][m % NB] = mfma32x32x16<DT>(fa[1][m / NB], fb[1][m % NB], acc[m / NB][m % NB]);
         if constexpr (m < L) load_one(off_next, int_c<slot2>{}, int_c<m>{});
         __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<(L > NMF ? L - NMF : 0)>([&](auto M) {   // loads beyond the slice's MFMAs
+        load_one(off_next, int_c<slot2>{}, int_c<NMF + decltype(M)::value>{});
       });
     }
     wait_lds();

@@ -10,9 +10,10 @@
 // codes by the FP8 MFMA, R = rounding to the 16-bit output dtype.
 //
 // Blocks of 128 or 256 rows run the LDS-tiled pass of grouped_gemm_tile.hpp
-// with one-byte operands: 64 reduction elements per chunk (64 bytes per row,
-// the 16-bit tile's layout), one v_mfma_scale_f32_32x32x64_f8f6f4 per
-// fragment pair, twice the MFMA throughput of the 16-bit path per byte of
+// with one-byte operands, its tile cut to the 64-row multiple that covers
+// the block's rows: 64 reduction elements per chunk (64 bytes per row, the
+// 16-bit tile's layout), one v_mfma_scale_f32_32x32x64_f8f6f4 per fragment
+// pair, twice the MFMA throughput of the 16-bit path per byte of
 // weights (the prefill layer and the hot experts of skewed routing are
 // compute-bound at 16 bits). Scheduling as in grouped_gemm_tile.hip: active
 // row blocks only, expert-local tile-major order dealt out to the XCDs in
@@ -51,7 +52,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_w8a8_kernel(GemmArgs g)
   const int m_start = g.group_offsets[e] + row_in_group;
   const int nchunks = g.kd / kRowB;      // one-byte elements: 64 per chunk
   const int rot = nt % nchunks;
-  tile_pass<DT, GATEUP, kRing, true>(g, lds, e, nt, m_start, rows, nchunks, rot, nullptr);
+  // A tile of 64 rows per row group of each wave, as few as the block needs
+  // (a 90-row block of a 256-row table computes 128 rows, not 256).
+  const int nq = (rows + 63) >> 6;
+  static_for<4>([&](auto I) {
+    constexpr int q = decltype(I)::value + 1;
+    // (a deeper ring for the smaller tiles, 6 chunks at 64 and 128 rows and
+    // 4 at 192, measured no faster: 3.61 against 3.56 ms at T = 4096)
+    if (nq == q) {
+      tile_pass<DT, GATEUP, kRing, true, q>(g, lds, e, nt, m_start, rows, nchunks, rot, nullptr);
+    }
+  });
 }
 
 template <int DT, bool GATEUP>

@@ -128,14 +128,16 @@ def test_down_reads_every_code_exactly():
     assert seen.size == 254
 
 
-@pytest.mark.parametrize("block_m", [32, 256])
-def test_down_exact_integer_sums(block_m):
+@pytest.mark.parametrize("block_m,P", [(32, 300), (256, 300), (128, 300), (256, 170),
+                                       (256, 100)])
+def test_down_exact_integer_sums(block_m, P):
     """Integer-valued codes (|v| <= 8) and power-of-two scales: every partial
-    sum is an exact fp32 integer, whatever the MFMA's order. 300 rows: at
-    block_m 256 one block of 256 rows (the LDS-tiled pass, both row halves)
-    and one of 44."""
-    rng = np.random.default_rng(4)
-    P, H, D = 300, 256, 512
+    sum is an exact fp32 integer, whatever the MFMA's order. The LDS-tiled
+    pass cuts its tile to 64, 128, 192 or 256 rows by the block's rows: 300
+    rows at block_m 256 are blocks of 256 and 44 rows, at 128 of 128, 128
+    and 44; 170 and 100 rows are one block each."""
+    rng = np.random.default_rng(4 + P)
+    H, D = 256, 512
     ints = {1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4a, 6: 0x4c, 7: 0x4e, 8: 0x50}
     def codes(shape):
         v = rng.integers(1, 9, size=shape)
