@@ -25,6 +25,13 @@
 //   moe_bench_driver copy BYTES [STEPS]
 //       A plain 16-byte-per-lane device copy of BYTES bytes (calibrates the
 //       FETCH_SIZE / WRITE_SIZE counters against a known transfer).
+//   moe_bench_driver read [STEPS]
+//       The device's read ceiling for the expert-weight stream: 4096
+//       workgroups of 256 threads each read 256 rows of 7168 bytes (7.5 GB in
+//       all), 16 bytes per thread and load with 32 loads in flight per
+//       thread and 96 KB of LDS reserved (one workgroup per CU, as the GEMM
+//       kernels run), once in 128-byte pieces of every row per step (the
+//       grouped GEMMs' weight pattern) and once in contiguous 4 KB pieces.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -104,6 +111,76 @@ __global__ void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ d
        i += static_cast<size_t>(gridDim.x) * blockDim.x) {
     dst[i] = src[i];
   }
+}
+
+// Read-only stream over disjoint slabs of 256 rows x RB bytes per workgroup
+// (see `read` above); the XOR of everything read is stored so nothing is
+// dropped.
+constexpr int kReadRowBytes = 7168;
+constexpr int kReadInflight = 32;
+template <bool LINEAR>
+__global__ __launch_bounds__(256) void read_kernel(const uint8_t* __restrict__ w, uint32_t* out) {
+  __shared__ uint8_t reserve[96 * 1024];
+  constexpr int kLoads = 8;                        // loads per step: 256 rows x 128 B
+  constexpr int kUnroll = kReadInflight / kLoads;  // steps per iteration
+  constexpr int kSteps = kReadRowBytes / 128;
+  static_assert(kSteps % kUnroll == 0, "whole iterations");
+  const int t = threadIdx.x;
+  const uint8_t* slab = w + static_cast<int64_t>(blockIdx.x) * 256 * kReadRowBytes;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int s0 = 0; s0 < kSteps; s0 += kUnroll) {
+    u32x4 v[kUnroll][kLoads];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int64_t off = LINEAR
+            ? (static_cast<int64_t>(s0 + u) * kLoads + i) * 4096 + t * 16
+            : static_cast<int64_t>(t / 8 + 32 * i) * kReadRowBytes + (s0 + u) * 128 + (t % 8) * 16;
+        v[u][i] = *reinterpret_cast<const u32x4*>(slab + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) acc ^= v[u][i];
+    }
+  }
+  if (t == 0) reserve[0] = static_cast<uint8_t>(acc.x);
+  out[static_cast<int64_t>(blockIdx.x) * 256 + t] = acc.x ^ acc.y ^ acc.z ^ acc.w ^ reserve[0];
+}
+
+int run_read(int steps) {
+  const int nwg = 4096;
+  const size_t bytes = static_cast<size_t>(nwg) * 256 * kReadRowBytes;
+  uint8_t* w = nullptr;
+  uint32_t* out = nullptr;
+  CHECK_HIP(hipMalloc(&w, bytes));
+  CHECK_HIP(hipMalloc(&out, static_cast<size_t>(nwg) * 256 * 4));
+  CHECK_HIP(hipMemset(w, 1, bytes));
+  hipEvent_t e0, e1;
+  CHECK_HIP(hipEventCreate(&e0));
+  CHECK_HIP(hipEventCreate(&e1));
+  for (int linear = 0; linear < 2; ++linear) {
+    for (int s = 0; s < steps; ++s) {
+      CHECK_HIP(hipEventRecord(e0, nullptr));
+      if (linear) {
+        hipLaunchKernelGGL(read_kernel<true>, dim3(nwg), dim3(256), 0, nullptr, w, out);
+      } else {
+        hipLaunchKernelGGL(read_kernel<false>, dim3(nwg), dim3(256), 0, nullptr, w, out);
+      }
+      CHECK_HIP(hipGetLastError());
+      CHECK_HIP(hipEventRecord(e1, nullptr));
+      CHECK_HIP(hipEventSynchronize(e1));
+      float ms = 0.0f;
+      CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+      std::printf("read %s %zu bytes: %.4f ms (%.1f GB/s)\n", linear ? "linear-4KB" : "rows-128B",
+                  bytes, ms, bytes / (ms * 1e6));
+    }
+  }
+  CHECK_HIP(hipFree(w));
+  CHECK_HIP(hipFree(out));
+  return 0;
 }
 
 void fill(uint16_t* p, size_t n, uint32_t seed, float scale, int dtype) {
@@ -403,9 +480,12 @@ int main(int argc, char** argv) {
   if (argc >= 3 && std::strcmp(argv[1], "copy") == 0) {
     return run_copy(std::strtoull(argv[2], nullptr, 10), argc >= 4 ? std::atoi(argv[3]) : 3);
   }
+  if (argc >= 2 && std::strcmp(argv[1], "read") == 0) {
+    return run_read(argc >= 3 ? std::atoi(argv[2]) : 5);
+  }
   std::fprintf(stderr,
                "usage: %s routing FILE [STEPS] [16bit|weighted|fp8|w8a8|w4a8|mx|fused] | reduce FILE [STEPS] "
-               "[bf16|fp8] | copy BYTES [STEPS]\n",
+               "[bf16|fp8] | copy BYTES [STEPS] | read [STEPS]\n",
                argv[0]);
   return 1;
 }
