@@ -1,7 +1,9 @@
-// The 256-row x 256-weight-row LDS tile pass of the grouped expert GEMMs
-// (shared by grouped_gemm_tile.hip, 16-bit operands, and
-// grouped_gemm_w8a8.hip, FP8 E4M3 operands). The design notes are in
-// grouped_gemm_tile.hip; with FP8 operands a chunk is 64 reduction elements
+// The LDS tile pass of the grouped expert GEMMs: 64 NQ activation rows
+// (NQ = 1..4 row groups per wave; 256 rows at NQ = 4) x 256 weight rows
+// (shared by grouped_gemm_tile.hip, 16-bit operands at NQ = 4, and
+// grouped_gemm_w8a8.hip, FP8 E4M3 operands with NQ cut to the block's rows).
+// The design notes are in grouped_gemm_tile.hip; with FP8 operands a chunk
+// is 64 reduction elements
 // (the same 64 bytes per row), and the two 16-byte fragments a lane reads
 // per chunk are together the 32-byte operand of one
 // v_mfma_scale_f32_32x32x64_f8f6f4 (lane half h supplies elements
@@ -18,9 +20,9 @@ namespace moe {
 namespace {
 
 constexpr int kRowB = 64;                       // bytes of one row per chunk
-constexpr int kTileRows = 256;                  // activation rows per tile
-constexpr int kABytes = kTileRows * kRowB;      // A part of one LDS buffer: 16 KB
-constexpr int kBufBytes = kABytes + 256 * kRowB;   // + 256 weight rows: 32 KB
+constexpr int kTileRows = 256;                  // activation rows of the largest tile (NQ = 4)
+constexpr int kABytes = kTileRows * kRowB;      // A part of its LDS buffer: 16 KB
+constexpr int kBufBytes = kABytes + 256 * kRowB;   // + 256 weight rows: 32 KB (LDS sizing)
 constexpr int kNBuf = 3;
 // Register-ring depth (chunks of loads in flight per thread, 8 loads each).
 constexpr int kRing = 3;
