@@ -108,10 +108,11 @@ constexpr int tile_buf_bytes() { return (64 * NQ + 256) * kRowB; }
 // does not have). R = register-ring depth. FP8: operands of one byte
 // (activations with a scale per row in g.sa, weights with a scale per row
 // in g.s0 / g.s1).
+// FP8: scale_s is an LDS array of 512 floats for the tile's row scales.
 template <int DT, bool GATEUP, int R, bool FP8 = false, int NQ = 4>
 __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e, int nt,
                                           int m_start, int rows, int nchunks, int rot,
-                                          const float* wrow) {
+                                          const float* wrow, float* scale_s = nullptr) {
   static_assert(NQ >= 1 && NQ <= 4, "row groups per wave");
   constexpr int EB = FP8 ? 1 : 2;          // bytes per operand element
   constexpr int NAL = NQ;                  // activation rows each thread loads per chunk
@@ -238,11 +239,30 @@ __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e
   // Prologue: chunks 0 .. R-1 in flight (each pinned in order by a scheduling
   // barrier: the loop's order); chunks 0 and 1 into buffers 0 and 1, each
   // followed by the load that reuses its slot; slice 0 of chunk 0.
+  // FP8: this thread's share of the tile's row scales -- activation row tid
+  // (< 64 NQ) and weight row tid -- loaded beside the first chunks and kept
+  // in registers until the epilogue (gate/up: the scale of row tid's token,
+  // its sorted_token read first, the dependent load after the chunk loads).
+  float sa_v = 0.0f, sw_v = 0.0f;
+  int tok = 0;
+  if constexpr (FP8) {
+    if constexpr (GATEUP) {
+      if (tid < 64 * NQ && tid < rows) tok = g.sorted_token[m_start + tid];
+      const float* sw = (tid < 128 ? g.s0 : g.s1) + static_cast<int64_t>(e) * g.n + nt * 128;
+      sw_v = sw[tid & 127];
+    } else {
+      if (tid < 64 * NQ && tid < rows) sa_v = g.sa[m_start + tid];
+      sw_v = g.s0[static_cast<int64_t>(e) * g.n + nt * 256 + tid];
+    }
+  }
   static_for<R>([&](auto S) {
     const int64_t off = chunk_off(decltype(S)::value);
     static_for<L>([&](auto I) { load_one(off, S, I); });
     __builtin_amdgcn_sched_barrier(0);
   });
+  if constexpr (FP8 && GATEUP) {
+    if (tid < 64 * NQ && tid < rows) sa_v = g.sa[tok];
+  }
   static_for<2>([&](auto C) {
     constexpr int c = decltype(C)::value;
     wait_vmcnt<kWait>();
@@ -325,45 +345,108 @@ __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e
 
   // Epilogue. Accumulator lane l holds column l % 32 of its 32 weight rows
   // and, in register i, row 8 (i / 4) + 4 (l / 32) + i % 4 of its 32 rows.
-  // FP8: each dot product times its activation row's scale, then its weight
-  // row's, left to right in fp32.
   const int lc = lane & 31;
   const int lh = lane >> 5;
   const bool weighted = !GATEUP && wrow != nullptr;
-  const float* s_w0 = FP8 ? g.s0 + static_cast<int64_t>(e) * g.n : nullptr;
-  const float* s_w1 = FP8 ? (GATEUP ? g.s1 : g.s0) + static_cast<int64_t>(e) * g.n : nullptr;
+  if constexpr (FP8) {
+    // Stored from the accumulators, that is one 2-byte store per value (64
+    // or 128 per row group and lane), each after a scale load; measured: a
+    // third of the T = 4096 down GEMM's time. Instead the tile's row scales
+    // go to LDS, and each wave rounds its sub-tile (32 NQ rows x kCols
+    // contiguous output columns) into a private LDS region, up to 2 row
+    // groups at a time, and stores whole 16-byte row pieces (16 lanes per
+    // 256 bytes of a row). The tile buffers are free: every wave passed the
+    // main loop's last barrier after its last fragment read. Each dot
+    // product times its activation row's scale, then its weight row's, left
+    // to right in fp32.
+    constexpr int kCols = GATEUP ? 64 : 128;     // output columns of a wave
+    constexpr int kStride = kCols + 8;           // rows 4 apart fall 16 banks apart
+    constexpr int kPassQ = NQ < 2 ? NQ : 2;      // row groups per pass
+    constexpr int kPieces = kPassQ * 32 * (kCols / 8) / 64;   // 16-byte pieces per lane and pass
+    static_assert(4 * kPassQ * 32 * kStride * 2 <= kNBuf * kBufBytes, "epilogue regions fit the LDS");
+    const int col_base = GATEUP ? nt * 128 + 64 * ch : nt * 256 + 128 * ch;
+    if (tid < 64 * NQ) scale_s[tid] = sa_v;
+    scale_s[256 + tid] = sw_v;
+    wait_lds();
+    barrier_no_wait();   // every thread's scales are visible
+    float s_w[NB];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
+    for (int j = 0; j < NB; ++j) s_w[j] = scale_s[256 + b_rows[j] + lc];
+    uint16_t* region = reinterpret_cast<uint16_t*>(lds) + wave * (kPassQ * 32 * kStride);
+    const bool c16 = (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+    static_for<(NQ + kPassQ - 1) / kPassQ>([&](auto PP) {
+      constexpr int q0 = decltype(PP)::value * kPassQ;
+      constexpr int nq = NQ - q0 < kPassQ ? NQ - q0 : kPassQ;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = a_row0 + 32 * q + 8 * (i >> 2) + 4 * lh + (i & 3);
-      if (row >= rows) continue;
-      uint16_t* out = g.c + static_cast<int64_t>(m_start + row) * g.n;
-      float s_a = 1.0f;
-      if constexpr (FP8) {
-        s_a = g.sa[GATEUP ? g.sorted_token[m_start + row] : m_start + row];
-      }
-      if constexpr (GATEUP) {
-        // gate fragment j pairs with up fragment j + NB / 2 (same h columns)
+      for (int qq = 0; qq < nq; ++qq) {
 #pragma unroll
-        for (int j = 0; j < NB / 2; ++j) {
-          const int col = nt * 128 + (b_rows[j] & 127) + lc;
-          float gv = acc[q][j][i], uv = acc[q][j + NB / 2][i];
-          if constexpr (FP8) {
-            gv = gv * s_a * s_w0[col];
-            uv = uv * s_a * s_w1[col];
+        for (int i = 0; i < 16; ++i) {
+          const int rl = 32 * qq + 8 * (i >> 2) + 4 * lh + (i & 3);
+          const int row = a_row0 + 32 * q0 + rl;
+          if (row >= rows) continue;
+          const float s_a = scale_s[row];
+          uint16_t* dst = region + rl * kStride + lc;
+          if constexpr (GATEUP) {
+            // gate fragment jj pairs with up fragment jj + NB / 2 (same h columns)
+#pragma unroll
+            for (int jj = 0; jj < NB / 2; ++jj) {
+              const float gv = acc[q0 + qq][jj][i] * s_a * s_w[jj];
+              const float uv = acc[q0 + qq][jj + NB / 2][i] * s_a * s_w[jj + NB / 2];
+              dst[32 * jj] = static_cast<uint16_t>(from_float<DT>(silu(gv) * uv));
+            }
+          } else {
+#pragma unroll
+            for (int jj = 0; jj < NB; ++jj) {
+              dst[32 * jj] =
+                  static_cast<uint16_t>(from_float<DT>(acc[q0 + qq][jj][i] * s_a * s_w[jj]));
+            }
           }
-          out[col] = static_cast<uint16_t>(from_float<DT>(silu(gv) * uv));
         }
-      } else {
-        const float w = weighted ? wrow[row] : 1.0f;
+      }
+      wait_lds();   // this wave's values are in its region
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int col = nt * 256 + b_rows[j] + lc;
-          float v = acc[q][j][i];
-          if constexpr (FP8) v = v * s_a * s_w0[col];
-          if (weighted) v *= w;
-          out[col] = static_cast<uint16_t>(from_float<DT>(v));
+      for (int p = 0; p < kPieces; ++p) {
+        const int idx = p * 64 + lane;
+        const int rl = idx / (kCols / 8);
+        const int cc = idx - rl * (kCols / 8);
+        const int row = a_row0 + 32 * q0 + rl;
+        if (rl < 32 * nq && row < rows) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(region + rl * kStride + cc * 8);
+          uint16_t* out = g.c + static_cast<int64_t>(m_start + row) * g.n + col_base + cc * 8;
+          if (c16) {
+            *reinterpret_cast<u32x4*>(out) = v;
+          } else {   // output not 16-byte aligned: the same values, 2 bytes at a time
+#pragma unroll
+            for (int k = 0; k < 8; ++k) out[k] = static_cast<uint16_t>(v[k >> 1] >> (16 * (k & 1)));
+          }
+        }
+      }
+      wait_lds();   // the reads are done before the next pass rewrites the region
+    });
+  } else {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = a_row0 + 32 * q + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (row >= rows) continue;
+        uint16_t* out = g.c + static_cast<int64_t>(m_start + row) * g.n;
+        if constexpr (GATEUP) {
+          // gate fragment j pairs with up fragment j + NB / 2 (same h columns)
+#pragma unroll
+          for (int j = 0; j < NB / 2; ++j) {
+            const int col = nt * 128 + (b_rows[j] & 127) + lc;
+            out[col] = static_cast<uint16_t>(from_float<DT>(silu(acc[q][j][i]) * acc[q][j + NB / 2][i]));
+          }
+        } else {
+          const float w = weighted ? wrow[row] : 1.0f;
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int col = nt * 256 + b_rows[j] + lc;
+            float v = acc[q][j][i];
+            if (weighted) v *= w;
+            out[col] = static_cast<uint16_t>(from_float<DT>(v));
+          }
         }
       }
     }

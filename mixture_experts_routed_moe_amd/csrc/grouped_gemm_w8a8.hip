@@ -32,6 +32,7 @@ namespace {
 template <int DT, bool GATEUP>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_w8a8_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kNBuf * kBufBytes];
+  __shared__ float scale_s[512];   // the tile's activation-row and weight-row scales
 
   const int total = g.active_count[0] * g.n_tiles;
   const int natural = tile_order_position(blockIdx.x, total, g.n_tiles);
@@ -60,7 +61,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_w8a8_kernel(GemmArgs g)
     // (a deeper ring for the smaller tiles, 6 chunks at 64 and 128 rows and
     // 4 at 192, measured no faster: 3.61 against 3.56 ms at T = 4096)
     if (nq == q) {
-      tile_pass<DT, GATEUP, kRing, true, q>(g, lds, e, nt, m_start, rows, nchunks, rot, nullptr);
+      tile_pass<DT, GATEUP, kRing, true, q>(g, lds, e, nt, m_start, rows, nchunks, rot, nullptr,
+                                            scale_s);
     }
   });
 }
