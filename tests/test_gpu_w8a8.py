@@ -90,16 +90,19 @@ def test_activation_quantizer_bit_exact(dtype):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), scales.view(np.uint32))
 
 
-def _down_exact(hq_codes, sh, w_codes, sw, block_m):
+def _down_exact(hq_codes, sh, w_codes, sw, block_m, out_shift=0):
     """moe_expert_down_w8a8 on given codes / scales (E = 1, every row to
-    expert 0) and the exact result, rounded to bf16."""
+    expert 0) and the exact result, rounded to bf16. out_shift: expert_out
+    starts that many elements into its allocation (2-byte steps off a
+    16-byte boundary)."""
     mr = _mr()
     P, D = hq_codes.shape
     H = w_codes.shape[0]
     ids = torch.zeros(P, 1, dtype=torch.int32, device=DEV)
     tables = mr.moe_dispatch(ids, None, 1, block_m=block_m)
     w8 = mr.FP8Weights(torch.from_numpy(w_codes[None]).to(DEV), torch.from_numpy(sw[None]).to(DEV))
-    eo = torch.full((P, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    buf = torch.full((P * H + out_shift,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    eo = buf[out_shift:].view(P, H)
     mr.moe_expert_down_w8a8(torch.from_numpy(hq_codes).to(DEV), torch.from_numpy(sh).to(DEV), w8,
                             tables, torch.bfloat16, expert_out=eo)
     torch.cuda.synchronize()
@@ -128,14 +131,16 @@ def test_down_reads_every_code_exactly():
     assert seen.size == 254
 
 
-@pytest.mark.parametrize("block_m,P", [(32, 300), (256, 300), (128, 300), (256, 170),
-                                       (256, 100)])
-def test_down_exact_integer_sums(block_m, P):
+@pytest.mark.parametrize("block_m,P,shift", [(32, 300, 0), (256, 300, 0), (128, 300, 0),
+                                             (256, 170, 0), (256, 100, 0), (256, 170, 1),
+                                             (128, 300, 3)])
+def test_down_exact_integer_sums(block_m, P, shift):
     """Integer-valued codes (|v| <= 8) and power-of-two scales: every partial
     sum is an exact fp32 integer, whatever the MFMA's order. The LDS-tiled
     pass cuts its tile to 64, 128, 192 or 256 rows by the block's rows: 300
     rows at block_m 256 are blocks of 256 and 44 rows, at 128 of 128, 128
-    and 44; 170 and 100 rows are one block each."""
+    and 44; 170 and 100 rows are one block each. A shifted expert_out (not
+    16-byte aligned) takes the tile epilogue's 2-byte stores."""
     rng = np.random.default_rng(4 + P)
     H, D = 256, 512
     ints = {1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4a, 6: 0x4c, 7: 0x4e, 8: 0x50}
@@ -146,7 +151,7 @@ def test_down_exact_integer_sums(block_m, P):
     hq, w = codes((P, D)), codes((H, D))
     sh = np.exp2(-rng.integers(0, 6, size=P)).astype(np.float32)
     sw = np.exp2(-rng.integers(0, 6, size=H)).astype(np.float32)
-    got, want = _down_exact(hq, sh, w, sw, block_m)
+    got, want = _down_exact(hq, sh, w, sw, block_m, out_shift=shift)
     assert np.array_equal(got, want)
 
 
