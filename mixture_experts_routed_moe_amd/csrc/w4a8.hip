@@ -205,6 +205,7 @@ struct W4GroupedArgs {
 template <int DT, bool GATEUP, int NAMAX>
 __global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][32 * NAMAX][kLdsRow];
+  __shared__ float sa_s[32 * NAMAX];   // the pass's activation-row scales
 
   const int total = g.active_count[0] * g.n_tiles;
   const int per_xcd = (total + 7) >> 3;
@@ -261,11 +262,21 @@ __global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g)
       const int64_t src = GATEUP ? g.sorted_token[m_start + r0 + r] : (m_start + r0 + r);
       asrc[q] = g.a + src * kd + a_seg * 16;
     }
+    // Row tid's activation scale, loaded now and used after the pass (a
+    // load per row in the epilogue -- through sorted_token for gate/up --
+    // put one or two memory latencies at the end of every pass).
+    float sa_mine = 0.0f;
+    if (tid < rows_pass) {
+      const int64_t row = m_start + r0 + tid;
+      sa_mine = g.sa[GATEUP ? g.sorted_token[row] : row];
+    }
     i32x16 acc[2 * NAMAX];
     auto epilogue = [&](auto NAC) __attribute__((always_inline)) {
       constexpr int na = decltype(NAC)::value;
       w4a8_pass<false, na, NAMAX, kStages>(asrc, a_row, a_seg, bptr, 0, nch, rot, rows_pass, lr, lh,
                                             lds, acc);
+      if (tid < rows_pass) sa_s[tid] = sa_mine;
+      __syncthreads();   // every row's scale is visible
 #pragma unroll
       for (int q = 0; q < na; ++q) {
 #pragma unroll
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void w4a8_grouped_kernel(W4GroupedArgs g)
           const int row = 32 * q + (i >> 2) * 8 + lh * 4 + (i & 3);
           if (row < rows_pass) {
             const int64_t out_row = m_start + r0 + row;
-            const float sa = g.sa[GATEUP ? g.sorted_token[out_row] : out_row];
+            const float sa = sa_s[row];
             uint16_t* out = g.c + out_row * g.n + col0 + lr;
             const float v0 = dequant(acc[2 * q][i] >> 4, sa, sw0);
             const float v1 = dequant(acc[2 * q + 1][i] >> 4, sa, sw1);
