@@ -149,4 +149,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // or global access is moved across it.
 __device__ __forceinline__ void barrier_no_wait() { asm volatile("s_barrier" ::: "memory"); }
 
+// Wait for this wave's outstanding LDS (and scalar memory) operations only:
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt at their "no wait" values.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 }  // namespace moe

@@ -83,7 +83,6 @@ __device__ __forceinline__ void wait_chunks(int after) {
   });
 }
 
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // FP8 E4M3 operands x FP8 E4M3 operands, fp32 accumulation: the scaled
 // MFMA with unit (E8M0 127 = 2^0) scales on both sides.
