@@ -244,7 +244,7 @@ def time_workload(cfg, steps, warmup, block_m, dev, flush, trials, weights="16bi
         quant_ms = ev[0].elapsed_time(ev[1])
         d["w_gate"], d["w_up"], d["w_down"] = q
     T, H, D, E, K = d["T"], d["H"], d["D"], d["E"], d["K"]
-    block_m = block_m or mr.default_block_m(T, K, E)
+    block_m = block_m or mr.default_block_m(T, K, E, weights)
     ids, w = d["topk_ids"], d["topk_weights"]
     x, wg, wu, wd = d["x"], d["w_gate"], d["w_up"], d["w_down"]
     tables = mr.MoeTables(T, K, E, block_m, dev)

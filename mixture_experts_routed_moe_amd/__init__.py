@@ -72,13 +72,23 @@ def _check_tensor(t, name, dtype=None, ndim=None, device=None):
     _require(t.is_contiguous(), MOE_ERR_SHAPE, "%s must be contiguous" % name)
 
 
-def default_block_m(T, K, E):
+# Largest row block worth building for each weight format: the W4A8 and MX
+# grouped kernels keep 128 / 64 rows per pass over the weights, and smaller
+# blocks let an expert's row blocks run side by side on one XCD and share
+# the weight reads in its L2 instead of re-reading them pass after pass
+# (measured at the DeepSeek prefill shape, T = 4096: W4A8 3.30 -> 3.20 ms at
+# 128, MX 3.88 -> 3.58 ms at 64).
+_BLOCK_M_CAP = {"w4a8": 128, "mx": 64}
+
+
+def default_block_m(T, K, E, weights="16bit"):
     """Row-block size of the tables: the power of two >= twice the mean rows
     per expert, clamped to [16, 256], so a typical expert fits in one block
-    and its weights are streamed once."""
+    and its weights are streamed once; for W4A8 and MX weights ("w4a8",
+    "mx") at most their kernels' pass height (128 / 64 rows)."""
     avg = max(1.0, T * K / E)
     bm = 1 << max(0, math.ceil(math.log2(2 * avg)))
-    return int(min(256, max(16, bm)))
+    return int(min(256, _BLOCK_M_CAP.get(weights, 256), max(16, bm)))
 
 
 class MoeTables:

@@ -142,6 +142,10 @@ def test_default_block_m():
     assert mr.default_block_m(4096, 8, 256) == 256
     assert mr.default_block_m(2048, 8, 256) == 128
     assert mr.default_block_m(1, 1, 256) == 16
+    assert mr.default_block_m(4096, 8, 256, "w4a8") == 128
+    assert mr.default_block_m(4096, 8, 256, "mx") == 64
+    assert mr.default_block_m(4096, 8, 256, "w8a8") == 256
+    assert mr.default_block_m(512, 8, 256, "mx") == 32
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

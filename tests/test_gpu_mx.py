@@ -237,7 +237,7 @@ def test_forward_mx_full_size_sampled(ci):
     cfg = S.CONFIGS[ci]
     d = S.make_moe_inputs(cfg, device=DEV)
     gpu, ref = _mx_weights(d)
-    block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"])
+    block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"], "mx")   # as the benchmark
     tables, h, eo, xq, xs, y = _run_mx(d, gpu, block_m=block_m)
     _check_x_quant(d, xq, xs)
     # one checked row in every scheduled row block (the MX oracle decodes

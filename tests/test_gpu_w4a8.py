@@ -249,7 +249,7 @@ def test_forward_w4a8_full_size_sampled(ci):
     cfg = S.CONFIGS[ci]
     d = S.make_moe_inputs(cfg, device=DEV)
     gpu, ref = _w4_weights(d)
-    block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"])
+    block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"], "w4a8")   # as the benchmark
     tables, h, eo, xq, sx, y = _run_w4(d, gpu, block_m=block_m)
     _check_x_quant(d, xq, sx)
     tokens = cover_tokens(d["topk_ids"].cpu().numpy(), cfg["E"], block_m, full_upto=0,
