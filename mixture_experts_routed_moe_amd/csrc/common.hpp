@@ -25,12 +25,14 @@ __device__ __forceinline__ float bf16_to_float(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// fp32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bfloat16, round to nearest even, with gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32; one instruction where the integer form
+// --- add 0x7fff plus the kept bit's lowest, shift, NaN select --- takes six,
+// a measurable share of the GEMM epilogues). Checked on MI355X against that
+// integer form on all 2^32 inputs: identical bits for every non-NaN input,
+// and NaN stays NaN.
 __device__ __forceinline__ uint32_t float_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ float f16_to_float(uint32_t b) {
