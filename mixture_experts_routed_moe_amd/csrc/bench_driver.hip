@@ -25,6 +25,13 @@
 //   moe_bench_driver copy BYTES [STEPS]
 //       A plain 16-byte-per-lane device copy of BYTES bytes (calibrates the
 //       FETCH_SIZE / WRITE_SIZE counters against a known transfer).
+//   moe_bench_driver bf16-rounding
+//       Checks the library's fp32 -> bf16 conversion (float_to_bf16 of
+//       common.hpp: gfx950's conversion instruction) against the integer
+//       round-to-nearest-even (add 0x7fff plus the lowest kept bit, keep the
+//       high half) on all 2^32 fp32 bit patterns; prints the non-NaN inputs
+//       whose bits differ and the NaN inputs whose result is not a NaN, and
+//       exits with status 0 only when both counts are 0.
 //   moe_bench_driver read [STEPS]
 //       The device's read ceiling for the expert-weight stream: 4096
 //       workgroups of 256 threads each read 256 rows of 7168 bytes (7.5 GB in
@@ -40,6 +47,7 @@
 #include <cstring>
 #include <vector>
 
+#include "common.hpp"
 #include "moe_routed.h"
 
 namespace {
@@ -181,6 +189,47 @@ int run_read(int steps) {
   CHECK_HIP(hipFree(w));
   CHECK_HIP(hipFree(out));
   return 0;
+}
+
+// Integer round-to-nearest-even fp32 -> bf16 (the reference of the check).
+__device__ uint32_t bf16_rne_integer(uint32_t u) { return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16; }
+
+__global__ void bf16_rounding_kernel(unsigned long long* counts, uint32_t* first_bad) {
+  unsigned long long bad = 0, bad_nan = 0;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  for (uint64_t x = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; x < (1ull << 32);
+       x += stride) {
+    const uint32_t u = static_cast<uint32_t>(x);
+    const uint32_t got = moe::float_to_bf16(__uint_as_float(u));
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      if ((got & 0x7fffu) <= 0x7f80u) ++bad_nan;
+    } else if (got != bf16_rne_integer(u)) {
+      ++bad;
+      atomicMin(first_bad, u);
+    }
+  }
+  atomicAdd(&counts[0], bad);
+  atomicAdd(&counts[1], bad_nan);
+}
+
+int run_bf16_rounding() {
+  unsigned long long* counts = nullptr;
+  uint32_t* first_bad = nullptr;
+  CHECK_HIP(hipMalloc(&counts, 2 * sizeof(unsigned long long)));
+  CHECK_HIP(hipMalloc(&first_bad, sizeof(uint32_t)));
+  CHECK_HIP(hipMemset(counts, 0, 2 * sizeof(unsigned long long)));
+  CHECK_HIP(hipMemset(first_bad, 0xff, sizeof(uint32_t)));
+  hipLaunchKernelGGL(bf16_rounding_kernel, dim3(8192), dim3(256), 0, nullptr, counts, first_bad);
+  CHECK_HIP(hipGetLastError());
+  unsigned long long h[2];
+  uint32_t first = 0;
+  CHECK_HIP(hipMemcpy(h, counts, sizeof(h), hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(&first, first_bad, sizeof(first), hipMemcpyDeviceToHost));
+  std::printf("bf16-rounding: non-NaN mismatches %llu (first input 0x%08x), NaN inputs not NaN %llu\n",
+              h[0], first, h[1]);
+  CHECK_HIP(hipFree(counts));
+  CHECK_HIP(hipFree(first_bad));
+  return (h[0] == 0 && h[1] == 0) ? 0 : 3;
 }
 
 void fill(uint16_t* p, size_t n, uint32_t seed, float scale, int dtype) {
@@ -480,12 +529,13 @@ int main(int argc, char** argv) {
   if (argc >= 3 && std::strcmp(argv[1], "copy") == 0) {
     return run_copy(std::strtoull(argv[2], nullptr, 10), argc >= 4 ? std::atoi(argv[3]) : 3);
   }
+  if (argc >= 2 && std::strcmp(argv[1], "bf16-rounding") == 0) return run_bf16_rounding();
   if (argc >= 2 && std::strcmp(argv[1], "read") == 0) {
     return run_read(argc >= 3 ? std::atoi(argv[2]) : 5);
   }
   std::fprintf(stderr,
                "usage: %s routing FILE [STEPS] [16bit|weighted|fp8|w8a8|w4a8|mx|fused] | reduce FILE [STEPS] "
-               "[bf16|fp8] | copy BYTES [STEPS] | read [STEPS]\n",
+               "[bf16|fp8] | copy BYTES [STEPS] | read [STEPS] | bf16-rounding\n",
                argv[0]);
   return 1;
 }
