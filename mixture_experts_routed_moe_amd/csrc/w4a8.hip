@@ -417,6 +417,32 @@ __global__ __launch_bounds__(256) void quantize_int8_rows_kernel(const void* __r
   }
 }
 
+// Eight 16-bit values (one 16-byte load): their largest magnitude, and
+// their int8 codes at scale s, packed in order.
+template <int DT>
+__device__ __forceinline__ float amax8_int(u32x4 w, float amax) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    amax = fmaxf(amax, fabsf(to_float<DT>(w[j] & 0xffffu)));
+    amax = fmaxf(amax, fabsf(to_float<DT>(w[j] >> 16)));
+  }
+  return amax;
+}
+
+template <int DT>
+__device__ __forceinline__ u32x2 encode8_int8(u32x4 w, float s) {
+  uint32_t packed[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t c0 = static_cast<uint32_t>(quant_code(to_float<DT>(w[j] & 0xffffu), s, -127.0f, 127.0f)) & 0xffu;
+    const uint32_t c1 = static_cast<uint32_t>(quant_code(to_float<DT>(w[j] >> 16), s, -127.0f, 127.0f)) & 0xffu;
+    const uint32_t pair = c0 | (c1 << 8);
+    if (j & 1) packed[j >> 1] |= pair << 16;
+    else packed[j >> 1] = pair;
+  }
+  return u32x2{packed[0], packed[1]};
+}
+
 // The same for 16-bit rows of a multiple of 8 values on a 16-byte aligned
 // base (the activations of the forward): each lane reads 8 values per
 // 16-byte load, the row's loads all in flight at once, and writes 8 codes
@@ -433,32 +459,70 @@ __global__ __launch_bounds__(256) void quantize_int8_rows16_kernel(const uint16_
   const int nvec = cols / 8;
   float amax = 0.0f;
 #pragma unroll 4
-  for (int v = lane; v < nvec; v += 64) {
-    const u32x4 w = row[v];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      amax = fmaxf(amax, fabsf(to_float<DT>(w[j] & 0xffffu)));
-      amax = fmaxf(amax, fabsf(to_float<DT>(w[j] >> 16)));
-    }
-  }
+  for (int v = lane; v < nvec; v += 64) amax = amax8_int<DT>(row[v], amax);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
   if (lane == 0) scales[r] = s;
   u32x2* out = reinterpret_cast<u32x2*>(q + r * cols);
 #pragma unroll 4
-  for (int v = lane; v < nvec; v += 64) {
-    const u32x4 w = row[v];
-    uint32_t packed[2];
+  for (int v = lane; v < nvec; v += 64) out[v] = encode8_int8<DT>(row[v], s);
+}
+
+// Rows of at most 512 NV values held in registers between the amax and the
+// encoding, so the row is read from memory once (with many rows in flight
+// per CU the two-pass form's second read mostly misses the cache).
+template <int DT, int NV>
+__global__ __launch_bounds__(256) void quantize_int8_rows_reg_kernel(const uint16_t* __restrict__ a,
+                                                                     int64_t rows, int cols,
+                                                                     int8_t* __restrict__ q,
+                                                                     float* __restrict__ scales) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;   // the whole wave exits together
+  const int lane = threadIdx.x & 63;
+  const u32x4* row = reinterpret_cast<const u32x4*>(a + r * cols);
+  const int nvec = cols / 8;
+  u32x4 w[NV];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t c0 = static_cast<uint32_t>(quant_code(to_float<DT>(w[j] & 0xffffu), s, -127.0f, 127.0f)) & 0xffu;
-      const uint32_t c1 = static_cast<uint32_t>(quant_code(to_float<DT>(w[j] >> 16), s, -127.0f, 127.0f)) & 0xffu;
-      const uint32_t pair = c0 | (c1 << 8);
-      if (j & 1) packed[j >> 1] |= pair << 16;
-      else packed[j >> 1] = pair;
-    }
-    out[v] = u32x2{packed[0], packed[1]};
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    w[i] = v < nvec ? row[v] : u32x4{0u, 0u, 0u, 0u};   // zeros leave the amax unchanged
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) amax = amax8_int<DT>(w[i], amax);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+  if (lane == 0) scales[r] = s;
+  u32x2* out = reinterpret_cast<u32x2*>(q + r * cols);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    if (v < nvec) out[v] = encode8_int8<DT>(w[i], s);
+  }
+}
+
+template <int DT>
+void launch_int8_rows16(const uint16_t* a, int64_t rows, int cols, int8_t* q, float* scales,
+                        dim3 grid, hipStream_t stream) {
+  const int nvec = cols / 8;   // 16-byte loads per row; the register form up to 16 per lane
+  auto reg = [&](auto NV) {
+    hipLaunchKernelGGL((quantize_int8_rows_reg_kernel<DT, decltype(NV)::value>), grid, dim3(256), 0, stream, a, rows,
+                       cols, q, scales);
+  };
+  if (nvec <= 64) {
+    reg(int_c<1>{});
+  } else if (nvec <= 128) {
+    reg(int_c<2>{});
+  } else if (nvec <= 256) {
+    reg(int_c<4>{});
+  } else if (nvec <= 512) {
+    reg(int_c<8>{});
+  } else if (nvec <= 1024) {
+    reg(int_c<16>{});
+  } else {
+    hipLaunchKernelGGL(quantize_int8_rows16_kernel<DT>, grid, dim3(256), 0, stream, a, rows, cols, q, scales);
   }
 }
 
@@ -489,11 +553,9 @@ hipError_t launch_quantize_int8_rows(const void* a, int64_t rows, int cols, int 
   const bool vec = dtype != kF32 && cols % 8 == 0 && reinterpret_cast<uintptr_t>(a) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(q) % 8 == 0;
   if (vec && dtype == kBF16) {
-    hipLaunchKernelGGL(quantize_int8_rows16_kernel<kBF16>, grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(a), rows, cols, q, scales);
+    launch_int8_rows16<kBF16>(static_cast<const uint16_t*>(a), rows, cols, q, scales, grid, stream);
   } else if (vec) {
-    hipLaunchKernelGGL(quantize_int8_rows16_kernel<kF16>, grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(a), rows, cols, q, scales);
+    launch_int8_rows16<kF16>(static_cast<const uint16_t*>(a), rows, cols, q, scales, grid, stream);
   } else if (dtype == kBF16) {
     hipLaunchKernelGGL(quantize_int8_rows_kernel<kBF16>, grid, dim3(256), 0, stream, a, rows, cols,
                        q, scales);

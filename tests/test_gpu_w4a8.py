@@ -47,7 +47,10 @@ def _rows_input(dtype, rows, cols, seed):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
-@pytest.mark.parametrize("cols", [2048, 7168, 2044])      # 2044: the scalar path
+# 16-bit rows of a multiple of 8 values are held in registers up to 8192
+# values (1, 2, ..., 16 loads per lane: 512 and 520 sit on either side of
+# the first step) and read twice beyond (8200); 2044: the scalar path.
+@pytest.mark.parametrize("cols", [2048, 7168, 2044, 512, 520, 8192, 8200])
 def test_quantize_int8_rows_bit_exact(dtype, cols):
     a = _rows_input(dtype, 37, cols, 1)
     q, s = _mr().quantize_int8_rows(a)

@@ -76,10 +76,13 @@ def _check_pairs(tables, h, eo, hp, ep):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_activation_quantizer_bit_exact(dtype):
+# Rows held in registers up to 8192 values (512 / 520: either side of the
+# first step of that form), read twice beyond (8200).
+@pytest.mark.parametrize("cols", [512, 520, 2048, 8192, 8200])
+def test_activation_quantizer_bit_exact(dtype, cols):
     mr = _mr()
-    g = torch.Generator().manual_seed(9)
-    a = torch.randn(37, 512, generator=g)
+    g = torch.Generator().manual_seed(9 + cols)
+    a = torch.randn(37, cols, generator=g)
     a[3] = 0.0
     a[5, ::3] *= 200.0
     a = a.to(dtype).to(DEV)
