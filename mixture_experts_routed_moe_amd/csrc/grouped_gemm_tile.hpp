@@ -362,7 +362,8 @@ __device__ __forceinline__ void tile_pass(const GemmArgs& g, uint8_t* lds, int e
     constexpr int kStride = kCols + 8;           // rows 4 apart fall 16 banks apart
     constexpr int kPassQ = NQ < 2 ? NQ : 2;      // row groups per pass
     constexpr int kPieces = kPassQ * 32 * (kCols / 8) / 64;   // 16-byte pieces per lane and pass
-    static_assert(4 * kPassQ * 32 * kStride * 2 <= kNBuf * kBufBytes, "epilogue regions fit the LDS");
+    // (callers allocate at least kNBuf buffers of this tile size)
+    static_assert(4 * kPassQ * 32 * kStride * 2 <= kNBuf * BufBytes, "epilogue regions fit the LDS");
     const int col_base = GATEUP ? nt * 128 + 64 * ch : nt * 256 + 128 * ch;
     if (tid < 64 * NQ) scale_s[tid] = sa_v;
     scale_s[256 + tid] = sw_v;

@@ -29,9 +29,9 @@
 namespace moe {
 namespace {
 
-template <int DT, bool GATEUP>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_w8a8_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kNBuf * kBufBytes];
+template <int DT, bool GATEUP, int NQMAX = 4>
+__global__ __launch_bounds__(kThreads, NQMAX <= 2 ? 2 : 1) void grouped_gemm_w8a8_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kNBuf * tile_buf_bytes<NQMAX>()];
   __shared__ float scale_s[512];   // the tile's activation-row and weight-row scales
 
   const int total = g.active_count[0] * g.n_tiles;
@@ -56,13 +56,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_w8a8_kernel(GemmArgs g)
   // A tile of 64 rows per row group of each wave, as few as the block needs
   // (a 90-row block of a 256-row table computes 128 rows, not 256).
   const int nq = (rows + 63) >> 6;
-  static_for<4>([&](auto I) {
+  static_for<NQMAX>([&](auto I) {
     constexpr int q = decltype(I)::value + 1;
     // (a deeper ring for the smaller tiles, 6 chunks at 64 and 128 rows and
     // 4 at 192, measured no faster: 3.61 against 3.56 ms at T = 4096)
     if (nq == q) {
-      tile_pass<DT, GATEUP, kRing, true, q>(g, lds, e, nt, m_start, rows, nchunks, rot, nullptr,
-                                            scale_s);
+      tile_pass<DT, GATEUP, NQMAX <= 2 ? 2 : kRing, true, q>(g, lds, e, nt, m_start, rows, nchunks,
+                                                             rot, nullptr, scale_s);
     }
   });
 }
@@ -101,6 +101,12 @@ hipError_t launch_w8a8_typed(const GemmProblem& p, const moe_tables& t, hipStrea
     } else {
       launch_rg<DT, 2, GATEUP, kStagesRG2, true, true>(grid, g, stream);
     }
+  } else if (t.block_m == 128) {
+    // blocks of <= 128 rows: the tile's instance for NQ <= 2 (72 KB of LDS,
+    // a 2-deep ring, 256 registers), two workgroups per CU
+    const unsigned tgrid = static_cast<unsigned>(tile_order_grid(total, g.n_tiles));
+    hipLaunchKernelGGL((grouped_gemm_w8a8_kernel<DT, GATEUP, 2>), dim3(tgrid), dim3(kThreads), 0,
+                       stream, g);
   } else {
     const unsigned tgrid = static_cast<unsigned>(tile_order_grid(total, g.n_tiles));
     hipLaunchKernelGGL((grouped_gemm_w8a8_kernel<DT, GATEUP>), dim3(tgrid), dim3(kThreads), 0,
