@@ -155,7 +155,7 @@ def test_forward_w8_full_size_sampled(ci):
     block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"])
     tables, h, eo, y = _run_w8(d, gpu, block_m=block_m)
     tokens = cover_tokens(d["topk_ids"].cpu().numpy(), cfg["E"], block_m, full_upto=0,
-                          group_rows=128)
+                          group_rows=128)   # a covering set: the whole decode workload is 100 s of oracle time
     y_ref = _oracle_w8(d, ref, tokens=tokens)
     got = y.float().cpu().numpy()
     assert not np.isnan(got).any()

@@ -255,8 +255,8 @@ def test_forward_w4a8_full_size_sampled(ci):
     block_m = mr.default_block_m(cfg["T"], cfg["K"], cfg["E"], "w4a8")   # as the benchmark
     tables, h, eo, xq, sx, y = _run_w4(d, gpu, block_m=block_m)
     _check_x_quant(d, xq, sx)
-    tokens = cover_tokens(d["topk_ids"].cpu().numpy(), cfg["E"], block_m, full_upto=0,
-                          group_rows=128)
+    tokens = cover_tokens(d["topk_ids"].cpu().numpy(), cfg["E"], block_m, full_upto=512,
+                          group_rows=128)   # the decode workload in full
     y_ref = _oracle_w4(d, ref, tokens=tokens)
     got = y.float().cpu().numpy()
     assert not np.isnan(got).any()
